@@ -1,0 +1,243 @@
+"""Benchmark of the embedding weight-gradient accumulation on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+One step = one whole call (sort, partial sums, long-run combine) over the
+headline workload: 8192 Zipf(1.1) token ids into a 129280 x 7168 fp32
+main_grad with a bf16 grad. Inputs are resident in HBM before timing. Before
+every step, outside its timed interval, a 1 GiB buffer is written so that
+neither L2 nor the 256 MB Infinity Cache holds the inputs. Each step is timed
+with HIP events recorded by the library on the launch stream around each of
+its three kernels.
+
+Prints one JSON line: value = algorithmic bytes / mean call time (GB/s),
+roofline of the dominant kernel (the partial-sum pass), and the CPU oracle
+timed on the host as cpu_baseline.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+FLUSH_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["partial_sums.hip", "ewg_device.h", "ewg_internal.h"]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="rough budget for the CPU oracle timing")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 256 MiB device copy (reference for counter scaling)")
+    return p.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its launch stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h.value
+        return arr
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_embedding_weight_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the partial-sum kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"partial_sums_{workload_name}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256:\s*(\w+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def cpu_baseline(w, ids_np, grad_np, budget_s):
+    """The oracle as it stands (single-threaded C), on the whole workload with
+    main_grad restricted to its touched rows (ids relabelled in order)."""
+    import oracle
+    import workloads as wl
+
+    rows = np.unique(ids_np)
+    compact = np.searchsorted(rows, ids_np).astype(np.int32)
+    rng = np.random.default_rng(0)
+    mg = wl.to_numpy_bits(wl.normal_tensor(rng, (rows.size, w.hidden), w.main_grad_sigma,
+                                           w.main_grad_dtype))
+    times = []
+    start = time.perf_counter()
+    while not times or (time.perf_counter() - start < budget_s and len(times) < 20):
+        m = mg.copy()
+        t0 = time.perf_counter()
+        oracle.accumulate_embedding_wgrad(compact, grad_np, m, w.grad_dtype, w.main_grad_dtype)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                          "(the path needs no collective and is not sharded here)"}))
+        sys.exit(2)
+
+    import torch
+
+    import sparse_embedding_weight_amd as ewg
+    from sparse_embedding_weight_amd import _binding as B
+    import workloads as wl
+
+    name = args.workload or wl.HEADLINE
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    ids_np = wl.make_ids(w).reshape(-1)
+    ids = torch.from_numpy(ids_np).to(dev)
+    grad_cpu = wl.make_grad(w).reshape(w.num_tokens, w.hidden)
+    grad = grad_cpu.to(dev)
+    mg = wl.make_main_grad(w, dev)
+    counts = np.bincount(ids_np, minlength=w.vocab)
+    uniq = int((counts > 0).sum())
+    u_long = int((counts > ewg.NROWS).sum())
+    u_short = uniq - u_long
+    sg = 2 if w.grad_dtype == "bf16" else 4
+    sm = 2 if w.main_grad_dtype == "bf16" else 4
+    alg_bytes = wl.algorithmic_bytes(w.num_tokens, w.hidden, uniq, w.grad_dtype,
+                                     w.main_grad_dtype, ids_np.itemsize)
+    # the partial-sum pass reads every grad row and updates the rows of single-chunk runs
+    ps_bytes = w.num_tokens * w.hidden * sg + 2 * u_short * w.hidden * sm
+
+    ws = torch.empty(ewg.workspace_bytes(w.num_tokens, w.hidden), dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    hip = HipEvents()
+    nsteps = args.warmup + args.steps
+    events = [hip.create(4) for _ in range(nsteps)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    call_args = (ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), w.num_tokens, w.hidden, w.vocab,
+                 grad.stride(0), mg.stride(0), B.DTYPE_CODE[ids.dtype], B.DTYPE_CODE[grad.dtype],
+                 B.DTYPE_CODE[mg.dtype], ws.data_ptr(), ws.numel(), stream)
+
+    torch.cuda.synchronize()
+    t_wall = None
+    for step in range(nsteps):
+        if step == args.warmup:
+            torch.cuda.synchronize()
+            t_wall = time.perf_counter()
+        flush.fill_(float(step))
+        st = B.lib.accumulate_embedding_wgrad_timed(*call_args, events[step])
+        if st != 0:
+            raise B.EmbeddingWgradError(st, "accumulate_embedding_wgrad_timed")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+
+    timed = events[args.warmup:]
+    t_sort = np.array([hip.ms(e[0], e[1]) for e in timed])
+    t_ps = np.array([hip.ms(e[1], e[2]) for e in timed])
+    t_lr = np.array([hip.ms(e[2], e[3]) for e in timed])
+    t_call = np.array([hip.ms(e[0], e[3]) for e in timed])
+    for e in events:
+        hip.destroy(e)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    mean_call_ms = float(t_call.mean())
+    value = alg_bytes / (mean_call_ms * 1e-3) / 1e9
+    ps_ms = float(t_ps.mean())
+    achieved = ps_bytes / (ps_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "us/call + achieved HBM GB/s, 8192 tokens into 129280x7168 main_grad",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_call_ms, 5),
+        "us_per_call": round(mean_call_ms * 1e3, 2),
+        "us_per_call_p10_p50_p90": [round(float(np.percentile(t_call, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "us_per_kernel": {"sort_tokens": round(float(t_sort.mean()) * 1e3, 2),
+                          "partial_sums": round(ps_ms * 1e3, 2),
+                          "long_run_sums": round(float(t_lr.mean()) * 1e3, 2)},
+        "wall_ms_per_step_incl_cache_flush": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "num_tokens": w.num_tokens, "vocab": w.vocab,
+                   "hidden": w.hidden, "ids": f"{w.ids_kind}" + (f"(s={w.zipf_s})" if w.ids_kind == "zipf" else ""),
+                   "grad_dtype": w.grad_dtype, "main_grad_dtype": w.main_grad_dtype,
+                   "distinct_ids": uniq, "runs_longer_than_10": u_long,
+                   "algorithmic_bytes": alg_bytes, "cache_flush_between_calls": True},
+        "roofline": {"bound": "hbm", "kernel": "partial_sums", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes_per_launch": ps_bytes,
+                     "traffic": measured_traffic(name)},
+    }
+
+    if not args.no_cpu_baseline:
+        t_cpu, reps = cpu_baseline(w, ids_np, wl.to_numpy_bits(grad_cpu), args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(alg_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds_per_call": round(t_cpu, 4),
+            "sample": f"the whole workload ({w.num_tokens} tokens, hidden {w.hidden}); main_grad "
+                      f"restricted to its {uniq} touched rows (ids relabelled in order); median of "
+                      f"{reps} calls of the single-threaded C oracle"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

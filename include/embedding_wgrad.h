@@ -1,0 +1,181 @@
+/*
+ * embedding_wgrad.h -- C ABI of the MI355X (gfx950) embedding weight-gradient
+ * accumulation library, libembedding_wgrad.so.
+ *
+ * Operation (Megatron-Core API docs, "core.fusions.fused_embedding_wgrad",
+ * accumulate_embedding_wgrad and the introduction):
+ *
+ *     main_grad += embedding_dense_backward(grad, ids)
+ *
+ * touching only the rows of main_grad whose id occurs in ids, with the
+ * arithmetic of the sort-based dense backward (introduction, first bullet)
+ * followed by main_grad.add_ (second bullet):
+ *   - token ids are sorted together with their positions;
+ *   - the grad rows of one id are summed in position order into fp32 partial
+ *     sums of at most 10 rows (chunks counted from the first row of the id);
+ *   - the partial sums are added in order starting from 0 and the total is
+ *     rounded once (round to nearest even) to grad's dtype;
+ *   - that value is added to the main_grad row in fp32 and the sum rounded to
+ *     main_grad's dtype.
+ * Rows of ids that do not occur are neither read nor written (the sentence
+ * after the two bullets). For given inputs every output bit is fixed: two
+ * calls on the same inputs give identical main_grad bits.
+ *
+ * Conventions for every entry point below:
+ *   - pointers named ids, grad, main_grad, workspace and the sort tables are
+ *     DEVICE pointers on the device that `stream` belongs to, owned by the
+ *     caller; the library keeps no pointer after the call returns;
+ *   - all work is enqueued on `stream` (NULL = the legacy default stream);
+ *     no entry point synchronises the stream or allocates device memory;
+ *   - arguments are checked on the host before anything is enqueued; on any
+ *     non-zero return nothing was enqueued and main_grad is untouched
+ *     (except EWG_HIP_ERROR, which reports a failed launch);
+ *   - the functions are thread-safe; concurrent calls must not share a
+ *     workspace unless ordered by their streams.
+ */
+#ifndef EMBEDDING_WGRAD_H
+#define EMBEDDING_WGRAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Envelope (page, Data: MIN_TOKENS, MAX_TOKENS, _NROWS). MIN_TOKENS is the
+ * first token count on PyTorch's sort-based path ("more than 3072 tokens"). */
+#define EWG_MIN_TOKENS 3073
+#define EWG_MAX_TOKENS 8192
+#define EWG_NROWS 10
+
+/* Element types. ids: EWG_INT32 or EWG_INT64. grad, main_grad: EWG_BF16 or EWG_FP32. */
+typedef enum ewg_dtype {
+    EWG_INT32 = 0,
+    EWG_INT64 = 1,
+    EWG_BF16 = 2,
+    EWG_FP32 = 3
+} ewg_dtype;
+
+typedef enum ewg_status {
+    EWG_OK = 0,
+    EWG_UNSUPPORTED = 1,          /* outside the envelope (can_accumulate... is 0) */
+    EWG_INVALID_ARGUMENT = 2,     /* null pointer, bad stride, bad dtype code */
+    EWG_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below ..._workspace_bytes() */
+    EWG_HIP_ERROR = 4             /* a kernel launch failed */
+} ewg_status;
+
+/*
+ * Number of low key bits that hold a token's position, for num_tokens tokens
+ * (page, _position_bits): the fewest bits that represent every position
+ * 0 .. num_tokens-1, i.e. bit_length(num_tokens - 1); 0 for num_tokens <= 1.
+ * Host only.
+ */
+int ewg_position_bits(int64_t num_tokens);
+
+/*
+ * Whether accumulate_embedding_wgrad supports these sizes and types (page,
+ * can_accumulate_embedding_wgrad): 1 or 0, host only, reads no memory.
+ * True iff
+ *   EWG_MIN_TOKENS <= num_tokens <= EWG_MAX_TOKENS (both bounds included),
+ *   hidden >= 1, num_embeddings >= 1,
+ *   ids_dtype is EWG_INT32 or EWG_INT64,
+ *   grad_dtype and main_grad_dtype are EWG_BF16 or EWG_FP32, and
+ *   the largest id and position pack into 31 bits:
+ *     ((num_embeddings - 1) << ewg_position_bits(num_tokens)) | (num_tokens - 1) < 2^31.
+ * (The page's "on the GPU" condition is the caller's: the pointers passed to
+ * accumulate_embedding_wgrad must be device memory.)
+ */
+int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                                   int ids_dtype, int grad_dtype, int main_grad_dtype);
+
+/*
+ * Bytes of device workspace accumulate_embedding_wgrad and
+ * accumulate_embedding_wgrad_sort_tokens need for these sizes (host only).
+ * The workspace holds the sorted chunk tables and the fp32 partial sums of
+ * runs longer than EWG_NROWS rows; its content between calls is not part of
+ * the interface except for the first 4 bytes (see below). 0 if the sizes are
+ * out of range.
+ */
+size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);
+
+/*
+ * main_grad[ids[p], :] += the weight gradient, touching only occurring rows
+ * (page, accumulate_embedding_wgrad).
+ *
+ *   ids        num_tokens ids (ids_dtype), the flattened (row-major) id tensor;
+ *              position p of a token is its index here. Each id must lie in
+ *              [0, num_embeddings). If any does not, the call changes nothing
+ *              in main_grad and stores the number of such ids as an int32 in
+ *              the first 4 bytes of the workspace (0 after a valid call).
+ *   grad       num_tokens rows of `hidden` values (grad_dtype); row p starts at
+ *              element p * grad_row_stride; unit column stride.
+ *   main_grad  num_embeddings rows of `hidden` values (main_grad_dtype); row v
+ *              starts at element v * main_grad_row_stride; unit column stride.
+ *              Updated in place; must not overlap grad, ids or the workspace.
+ *   grad_row_stride, main_grad_row_stride
+ *              in elements, each >= hidden.
+ *   workspace  device scratch of at least
+ *              accumulate_embedding_wgrad_workspace_bytes(num_tokens, hidden)
+ *              bytes, 256-byte aligned; it must not be used by another call
+ *              until this one has finished on `stream`.
+ *
+ * Returns EWG_OK after enqueueing three kernels on `stream`: the LDS radix
+ * sort with run marking, the partial-sum pass over the grad rows (which also
+ * finishes runs of at most EWG_NROWS rows), and the ordered combine of longer
+ * runs. Any alignment is accepted; 16-byte aligned rows take the vector path.
+ */
+int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_grad,
+                               int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                               int64_t grad_row_stride, int64_t main_grad_row_stride,
+                               int ids_dtype, int grad_dtype, int main_grad_dtype,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * accumulate_embedding_wgrad with timing markers: `events` points to 4
+ * caller-created hipEvent_t, recorded on `stream` before the sort kernel,
+ * before the partial-sum kernel, before the long-run kernel and after it.
+ * Same arguments, results and errors otherwise; meant for benchmarks.
+ */
+int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *main_grad,
+                                     int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                                     int64_t grad_row_stride, int64_t main_grad_row_stride,
+                                     int ids_dtype, int grad_dtype, int main_grad_dtype,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream, hipEvent_t *events);
+
+/*
+ * Only the sort step, with its tables written out for inspection (page,
+ * _sort_tokens_kernel: sort the (token, position) pairs, give every sorted
+ * slot the first and last slot of its token's run, list the runs longer than
+ * NROWS with their count first). Device int32 outputs, s = sorted slot:
+ *   sorted_ids[s], positions[s]   num_tokens entries each
+ *   run_first[s], run_last[s]     first and last (inclusive) slot of the run
+ *   long_runs                     num_tokens + 1 entries: [0] = number of runs
+ *                                 longer than EWG_NROWS, [1..] their first
+ *                                 slots in ascending order
+ *   chunk_first                   num_tokens + 1 entries: [0] = number of
+ *                                 chunks, [1..] the first slot of every chunk
+ *                                 (chunks of EWG_NROWS rows counted from the
+ *                                 start of each run), ascending
+ * Entries past the counts are left as they were. Same envelope, id rule and
+ * workspace as accumulate_embedding_wgrad (with invalid ids both counts are 0).
+ */
+int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,
+                                           int64_t num_embeddings, int ids_dtype,
+                                           int32_t *sorted_ids, int32_t *positions,
+                                           int32_t *run_first, int32_t *run_last,
+                                           int32_t *long_runs, int32_t *chunk_first,
+                                           void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char *ewg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMBEDDING_WGRAD_H */

@@ -1,0 +1,22 @@
+"""MI355X (gfx950) embedding weight-gradient accumulation.
+
+    main_grad += embedding_dense_backward(grad, ids), touching only the rows of ids
+
+with the arithmetic of PyTorch's sort-based embedding backward followed by
+main_grad.add_ (Megatron-Core API docs, "core.fusions.fused_embedding_wgrad").
+The work runs in hand-written HIP kernels behind the C ABI of
+include/embedding_wgrad.h; this package is a thin binding to it.
+"""
+from ._binding import (  # noqa: F401
+    MAX_TOKENS,
+    MIN_TOKENS,
+    NROWS,
+    EmbeddingWgradError,
+    accumulate_embedding_wgrad,
+    can_accumulate_embedding_wgrad,
+    invalid_id_count,
+    position_bits,
+    sort_tokens,
+    workspace_bytes,
+)
+from ._binding import LIBRARY as library_path  # noqa: F401

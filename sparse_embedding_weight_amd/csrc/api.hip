@@ -1,0 +1,199 @@
+// Host side of the C ABI declared in include/embedding_wgrad.h: argument
+// checks, workspace layout, vector-path selection and the three launches.
+// Nothing here touches device memory or synchronises; every launch goes on
+// the caller's stream.
+#include "embedding_wgrad.h"
+
+#include <atomic>
+
+#include "ewg_internal.h"
+
+namespace {
+
+using namespace ewg;
+
+// Implementation limit on hidden: keeps (chunks x column tiles) in 32 bits.
+constexpr int64_t kMaxHidden = int64_t(1) << 24;
+
+int bit_length(uint64_t x) {
+    int b = 0;
+    while (x) {
+        ++b;
+        x >>= 1;
+    }
+    return b;
+}
+
+bool is_index_dtype(int d) { return d == EWG_INT32 || d == EWG_INT64; }
+bool is_float_dtype(int d) { return d == EWG_BF16 || d == EWG_FP32; }
+bool is_known_dtype(int d) { return d >= EWG_INT32 && d <= EWG_FP32; }
+size_t float_size(int d) { return d == EWG_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, int64_t row_stride_bytes, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a == 0) && (row_stride_bytes % (int64_t)a == 0);
+}
+
+// Compute units of the current device, cached per device ordinal.
+int num_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+int check_common(int64_t num_tokens, int64_t hidden, int64_t num_embeddings, int ids_dtype,
+                 int grad_dtype, int main_grad_dtype) {
+    if (!is_known_dtype(ids_dtype) || !is_known_dtype(grad_dtype) || !is_known_dtype(main_grad_dtype))
+        return EWG_INVALID_ARGUMENT;
+    if (!can_accumulate_embedding_wgrad(num_tokens, hidden, num_embeddings, ids_dtype, grad_dtype,
+                                        main_grad_dtype))
+        return EWG_UNSUPPORTED;
+    return EWG_OK;
+}
+
+int check_workspace(const void *workspace, size_t workspace_bytes, int64_t num_tokens,
+                    int64_t hidden) {
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return EWG_INVALID_ARGUMENT;
+    if (workspace_bytes < ws_layout(num_tokens, hidden).total) return EWG_WORKSPACE_TOO_SMALL;
+    return EWG_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? EWG_OK : EWG_HIP_ERROR; }
+
+int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_tokens,
+               int64_t hidden, int64_t num_embeddings, int64_t grad_row_stride,
+               int64_t main_grad_row_stride, int ids_dtype, int grad_dtype, int main_grad_dtype,
+               void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
+    int st = check_common(num_tokens, hidden, num_embeddings, ids_dtype, grad_dtype, main_grad_dtype);
+    if (st != EWG_OK) return st;
+    if (!ids || !grad || !main_grad) return EWG_INVALID_ARGUMENT;
+    if (grad_row_stride < hidden || main_grad_row_stride < hidden) return EWG_INVALID_ARGUMENT;
+    st = check_workspace(workspace, workspace_bytes, num_tokens, hidden);
+    if (st != EWG_OK) return st;
+
+    const bool g_bf16 = grad_dtype == EWG_BF16, m_bf16 = main_grad_dtype == EWG_BF16;
+    const size_t gs = float_size(grad_dtype), ms = float_size(main_grad_dtype);
+    // partial-sum kernel: a lane moves 16 bytes of grad and the same columns of main_grad
+    const int vec_g = (int)(16 / gs);
+    const bool vec2 = aligned(grad, grad_row_stride * (int64_t)gs, 16) &&
+                      aligned(main_grad, main_grad_row_stride * (int64_t)ms,
+                              vec_g * ms < 16 ? vec_g * ms : 16);
+    // long-run kernel: a lane moves 4 fp32 partial sums and 4 main_grad columns
+    const bool vec3 = aligned(main_grad, main_grad_row_stride * (int64_t)ms, 4 * ms < 16 ? 4 * ms : 16);
+
+    const WsLayout l = ws_layout(num_tokens, hidden);
+    const int n = (int)num_tokens;
+    const int pos_bits = ewg_position_bits(num_tokens);
+    const int id_bits = bit_length((uint64_t)(num_embeddings - 1));
+    const int cus = num_cus();
+    const SortTables no_tables = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+
+    (void)hipGetLastError();   // start from a clean per-thread error state
+    if (events && hipEventRecord(events[0], stream) != hipSuccess) return EWG_HIP_ERROR;
+    st = to_status(launch_sort_tokens(ids, ids_dtype == EWG_INT64, n, (int)num_embeddings, pos_bits,
+                                      id_bits, workspace, l, no_tables, stream));
+    if (st != EWG_OK) return st;
+    if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
+    st = to_status(launch_partial_sums(g_bf16, m_bf16, vec2, grad, grad_row_stride, main_grad,
+                                       main_grad_row_stride, (int)hidden, workspace, l, n, cus,
+                                       stream));
+    if (st != EWG_OK) return st;
+    if (events && hipEventRecord(events[2], stream) != hipSuccess) return EWG_HIP_ERROR;
+    st = to_status(launch_long_run_sums(g_bf16, m_bf16, vec3, main_grad, main_grad_row_stride,
+                                        (int)hidden, workspace, l, n / 11, cus, stream));
+    if (st != EWG_OK) return st;
+    if (events && hipEventRecord(events[3], stream) != hipSuccess) return EWG_HIP_ERROR;
+    return EWG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ewg_position_bits(int64_t num_tokens) {
+    return num_tokens <= 1 ? 0 : bit_length((uint64_t)(num_tokens - 1));
+}
+
+int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                                   int ids_dtype, int grad_dtype, int main_grad_dtype) {
+    if (num_tokens < EWG_MIN_TOKENS || num_tokens > EWG_MAX_TOKENS) return 0;
+    if (hidden < 1 || hidden > kMaxHidden || num_embeddings < 1) return 0;
+    if (!is_index_dtype(ids_dtype) || !is_float_dtype(grad_dtype) || !is_float_dtype(main_grad_dtype))
+        return 0;
+    const int pb = ewg_position_bits(num_tokens);
+    // ((num_embeddings - 1) << pb) | (num_tokens - 1) < 2^31
+    if (num_embeddings - 1 >= (int64_t(1) << (31 - pb))) return 0;
+    return 1;
+}
+
+size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden) {
+    if (num_tokens < 1 || num_tokens > EWG_MAX_TOKENS || hidden < 1 || hidden > kMaxHidden) return 0;
+    return ws_layout(num_tokens, hidden).total;
+}
+
+int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_grad,
+                               int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                               int64_t grad_row_stride, int64_t main_grad_row_stride,
+                               int ids_dtype, int grad_dtype, int main_grad_dtype,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, grad_row_stride,
+                      main_grad_row_stride, ids_dtype, grad_dtype, main_grad_dtype, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *main_grad,
+                                     int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
+                                     int64_t grad_row_stride, int64_t main_grad_row_stride,
+                                     int ids_dtype, int grad_dtype, int main_grad_dtype,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream, hipEvent_t *events) {
+    if (!events) return EWG_INVALID_ARGUMENT;
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, grad_row_stride,
+                      main_grad_row_stride, ids_dtype, grad_dtype, main_grad_dtype, workspace,
+                      workspace_bytes, stream, events);
+}
+
+int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,
+                                           int64_t num_embeddings, int ids_dtype,
+                                           int32_t *sorted_ids, int32_t *positions,
+                                           int32_t *run_first, int32_t *run_last,
+                                           int32_t *long_runs, int32_t *chunk_first,
+                                           void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+    if (!is_known_dtype(ids_dtype)) return EWG_INVALID_ARGUMENT;
+    if (!can_accumulate_embedding_wgrad(num_tokens, 1, num_embeddings, ids_dtype, EWG_FP32, EWG_FP32))
+        return EWG_UNSUPPORTED;
+    if (!ids || !sorted_ids || !positions || !run_first || !run_last || !long_runs || !chunk_first)
+        return EWG_INVALID_ARGUMENT;
+    // the sort step uses only the table part of the workspace, which does not depend on hidden
+    int st = check_workspace(workspace, workspace_bytes, num_tokens, 1);
+    if (st != EWG_OK) return st;
+    const WsLayout l = ws_layout(num_tokens, 1);
+    const SortTables tables = {sorted_ids, positions, run_first, run_last, long_runs, chunk_first};
+    (void)hipGetLastError();
+    return to_status(launch_sort_tokens(ids, ids_dtype == EWG_INT64, (int)num_tokens,
+                                        (int)num_embeddings, ewg_position_bits(num_tokens),
+                                        bit_length((uint64_t)(num_embeddings - 1)), workspace, l,
+                                        tables, stream));
+}
+
+const char *ewg_status_string(int status) {
+    switch (status) {
+        case EWG_OK: return "success";
+        case EWG_UNSUPPORTED: return "unsupported: outside the envelope of can_accumulate_embedding_wgrad";
+        case EWG_INVALID_ARGUMENT: return "invalid argument (null pointer, stride below hidden, unknown dtype code or misaligned workspace)";
+        case EWG_WORKSPACE_TOO_SMALL: return "workspace smaller than accumulate_embedding_wgrad_workspace_bytes()";
+        case EWG_HIP_ERROR: return "HIP error while enqueueing a kernel";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

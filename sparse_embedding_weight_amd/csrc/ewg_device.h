@@ -1,0 +1,99 @@
+// Device helpers of libembedding_wgrad.so: element types, rounding, and
+// 16-byte vector loads/stores. Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ewg {
+
+// fp32 -> bf16, round to nearest, ties to even. Adding 0x7fff plus the lowest
+// kept bit to the dropped half carries into the kept half exactly when the
+// dropped half is above one half ulp, or equal to it with an odd kept half; a
+// carry out of the mantissa moves into the exponent (largest values -> inf).
+// NaN keeps its sign and becomes quiet.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// Element type tags: storage type, widening to fp32, rounding from fp32.
+struct BF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float widen(T v) { return bf16_to_f32(v); }
+    static __device__ __forceinline__ T narrow(float x) { return f32_to_bf16_rne(x); }
+    // the fp32 value of narrow(x)
+    static __device__ __forceinline__ float round(float x) { return bf16_to_f32(f32_to_bf16_rne(x)); }
+};
+
+struct F32 {
+    using T = float;
+    static __device__ __forceinline__ float widen(T v) { return v; }
+    static __device__ __forceinline__ T narrow(float x) { return x; }
+    static __device__ __forceinline__ float round(float x) { return x; }
+};
+
+// Load / store N consecutive elements. The address must be aligned to
+// min(16, N * sizeof(T)) bytes; wider groups are moved as 16-byte pieces.
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T *__restrict__ p, T (&out)[N]) {
+    constexpr int bytes = N * (int)sizeof(T);
+    if constexpr (bytes >= 16) {
+        static_assert(bytes % 16 == 0, "vector group must be a multiple of 16 bytes");
+#pragma unroll
+        for (int k = 0; k < bytes / 16; ++k) {
+            uint4 w = reinterpret_cast<const uint4 *>(p)[k];
+            __builtin_memcpy(reinterpret_cast<char *>(out) + 16 * k, &w, 16);
+        }
+    } else if constexpr (bytes == 8) {
+        uint2 w = *reinterpret_cast<const uint2 *>(p);
+        __builtin_memcpy(out, &w, 8);
+    } else if constexpr (bytes == 4) {
+        uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+        __builtin_memcpy(out, &w, 4);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) out[k] = p[k];
+    }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_vec(T *__restrict__ p, const T (&v)[N]) {
+    constexpr int bytes = N * (int)sizeof(T);
+    if constexpr (bytes >= 16) {
+        static_assert(bytes % 16 == 0, "vector group must be a multiple of 16 bytes");
+#pragma unroll
+        for (int k = 0; k < bytes / 16; ++k) {
+            uint4 w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(v) + 16 * k, 16);
+            reinterpret_cast<uint4 *>(p)[k] = w;
+        }
+    } else if constexpr (bytes == 8) {
+        uint2 w;
+        __builtin_memcpy(&w, v, 8);
+        *reinterpret_cast<uint2 *>(p) = w;
+    } else if constexpr (bytes == 4) {
+        uint32_t w;
+        __builtin_memcpy(&w, v, 4);
+        *reinterpret_cast<uint32_t *>(p) = w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) p[k] = v[k];
+    }
+}
+
+// Finish one element of a run: total = the ordered sum of its chunk sums.
+// Round once to grad's dtype, add to main_grad in fp32, round to its dtype.
+template <typename G, typename M>
+__device__ __forceinline__ typename M::T finish(float total, typename M::T old) {
+    float g = G::round(total);
+    return M::narrow(M::widen(old) + g);
+}
+
+}  // namespace ewg

@@ -1,0 +1,124 @@
+"""Host-side tests of the C ABI (no GPU work): the library loads, exports every
+function include/embedding_wgrad.h declares, and its envelope and argument
+checks answer as the header says without enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_embedding_weight_amd as ewg
+from sparse_embedding_weight_amd import _binding as B
+
+HEADER_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return [n for n in names if n not in ("defined",)]
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) >= 7
+    for name in names:
+        assert hasattr(B.lib, name), f"{name} not exported by {B.LIBRARY}"
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_position_bits():
+    assert ewg.position_bits(1) == 0
+    assert ewg.position_bits(2) == 1
+    assert ewg.position_bits(3073) == 12
+    assert ewg.position_bits(4096) == 12
+    assert ewg.position_bits(4097) == 13
+    assert ewg.position_bits(8192) == 13
+
+
+def can(n, h=128, v=1000, i=B.EWG_INT32, g=B.EWG_BF16, m=B.EWG_FP32):
+    return B.lib.can_accumulate_embedding_wgrad(n, h, v, i, g, m)
+
+
+def test_envelope_token_bounds_inclusive():
+    assert can(3073) and can(8192)
+    assert not can(3072) and not can(8193) and not can(0)
+
+
+def test_envelope_dtypes():
+    for g in (B.EWG_BF16, B.EWG_FP32):
+        for m in (B.EWG_BF16, B.EWG_FP32):
+            for i in (B.EWG_INT32, B.EWG_INT64):
+                assert can(4096, i=i, g=g, m=m)
+    assert not can(4096, i=B.EWG_BF16)
+    assert not can(4096, g=B.EWG_INT32)
+    assert not can(4096, m=B.EWG_INT64)
+
+
+def test_envelope_31_bit_packing():
+    # N = 8192 -> 13 position bits -> ids < 2^18; N = 4096 -> 12 bits -> ids < 2^19
+    assert can(8192, v=1 << 18) and not can(8192, v=(1 << 18) + 1)
+    assert can(4096, v=1 << 19) and not can(4096, v=(1 << 19) + 1)
+    assert can(8192, v=129280)
+    assert not can(8192, v=0) and not can(8192, h=0)
+
+
+def test_workspace_bytes():
+    assert ewg.workspace_bytes(8192, 7168) > 2 * 8192 // 11 * 7168 * 4
+    assert ewg.workspace_bytes(0, 7) == 0 and ewg.workspace_bytes(8193, 7) == 0
+    assert ewg.workspace_bytes(4096, 1) < ewg.workspace_bytes(4096, 1000)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.lib.ewg_status_string(s)
+    assert b"unknown" in B.lib.ewg_status_string(99)
+
+
+def call(**kw):
+    a = dict(ids=8, grad=16, main_grad=32, n=4096, h=64, v=100, gs=64, ms=64,
+             i=B.EWG_INT32, g=B.EWG_BF16, m=B.EWG_FP32, ws=256 * 1024, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return B.lib.accumulate_embedding_wgrad(a["ids"], a["grad"], a["main_grad"], a["n"], a["h"],
+                                            a["v"], a["gs"], a["ms"], a["i"], a["g"], a["m"],
+                                            a["ws"], a["wsb"], a["stream"])
+
+
+def test_argument_errors_return_before_any_launch():
+    # every case fails a host check, so nothing touches a device
+    assert call(n=3072) == B.EWG_UNSUPPORTED
+    assert call(v=1 << 20, n=8192) == B.EWG_UNSUPPORTED
+    assert call(i=7) == B.EWG_INVALID_ARGUMENT
+    assert call(g=-1) == B.EWG_INVALID_ARGUMENT
+    assert call(ids=None) == B.EWG_INVALID_ARGUMENT
+    assert call(grad=None) == B.EWG_INVALID_ARGUMENT
+    assert call(main_grad=None) == B.EWG_INVALID_ARGUMENT
+    assert call(gs=63) == B.EWG_INVALID_ARGUMENT
+    assert call(ms=10) == B.EWG_INVALID_ARGUMENT
+    assert call(ws=None) == B.EWG_INVALID_ARGUMENT
+    assert call(ws=256 * 1024 + 8) == B.EWG_INVALID_ARGUMENT      # not 256-byte aligned
+    assert call(wsb=ewg.workspace_bytes(4096, 64) - 1) == B.EWG_WORKSPACE_TOO_SMALL
+    ev = (ctypes.c_void_p * 4)()
+    assert B.lib.accumulate_embedding_wgrad_timed(8, 16, 32, 4096, 64, 100, 64, 64, 0, 2, 3,
+                                                  256 * 1024, 1 << 30, None, None) == B.EWG_INVALID_ARGUMENT
+    assert B.lib.accumulate_embedding_wgrad_timed(8, 16, 32, 100, 64, 100, 64, 64, 0, 2, 3,
+                                                  256 * 1024, 1 << 30, None, ev) == B.EWG_UNSUPPORTED
+    sort = B.lib.accumulate_embedding_wgrad_sort_tokens
+    assert sort(8, 4096, 100, 5, *([8] * 6), 256 * 1024, 1 << 30, None) == B.EWG_INVALID_ARGUMENT
+    assert sort(8, 100, 100, 0, *([8] * 6), 256 * 1024, 1 << 30, None) == B.EWG_UNSUPPORTED
+    assert sort(8, 4096, 100, 0, *([8] * 5), None, 256 * 1024, 1 << 30, None) == B.EWG_INVALID_ARGUMENT
+    assert sort(8, 4096, 100, 0, *([8] * 6), 256 * 1024, 100, None) == B.EWG_WORKSPACE_TOO_SMALL
+
+
+def test_python_predicate_on_cpu_tensors_is_false():
+    ids = torch.zeros(4096, dtype=torch.int32)
+    grad = torch.zeros(4096, 8, dtype=torch.bfloat16)
+    mg = torch.zeros(10, 8, dtype=torch.float32)
+    assert not ewg.can_accumulate_embedding_wgrad(ids, grad, mg)
+    with pytest.raises(ValueError):
+        ewg.accumulate_embedding_wgrad(ids, grad, mg)

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP library against the CPU oracle, bit for bit.
+
+Every case runs the library through its C ABI (via the thin binding) on the
+GPU, copies the touched main_grad rows back, runs the oracle on the same
+inputs and compares the bits. Rows whose id does not occur must be
+bit-identical to a copy taken before the call. NaNs are compared as a class
+(their payload is not part of the definition).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ewg = pytest.importorskip("sparse_embedding_weight_amd")
+
+
+@pytest.fixture(autouse=True)
+def _gpu(require_gpu):
+    yield
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _is_nan_bits(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return (a & 0x7FFF) > 0x7F80
+    b = a.view(np.uint32)
+    return (b & 0x7FFFFFFF) > 0x7F800000
+
+
+def oracle_rows(ids: torch.Tensor, grad: torch.Tensor, rows: torch.Tensor,
+                before_rows: torch.Tensor) -> np.ndarray:
+    """Oracle result for the touched rows: ids relabelled to their index in the
+    sorted list of touched rows (an order-preserving relabel)."""
+    g_dt = "bf16" if grad.dtype == torch.bfloat16 else "fp32"
+    m_dt = "bf16" if before_rows.dtype == torch.bfloat16 else "fp32"
+    ids_np = ids.reshape(-1).cpu().numpy()
+    compact = np.searchsorted(rows.cpu().numpy(), ids_np).astype(ids_np.dtype)
+    grad_np = wl.to_numpy_bits(grad.reshape(ids_np.size, grad.shape[-1]).cpu())
+    mg_np = wl.to_numpy_bits(before_rows.cpu()).copy()
+    oracle.accumulate_embedding_wgrad(compact, grad_np, mg_np, g_dt, m_dt)
+    return mg_np
+
+
+def check_call(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor, **kw):
+    """Run one call on the GPU and compare with the oracle; returns the touched rows."""
+    m_dt = "bf16" if main_grad.dtype == torch.bfloat16 else "fp32"
+    rows = torch.unique(ids.reshape(-1).long())
+    before_rows = main_grad[rows].clone()
+    before = main_grad.clone()
+    ewg.accumulate_embedding_wgrad(ids, grad, main_grad, **kw)
+    torch.cuda.synchronize()
+
+    got = wl.to_numpy_bits(main_grad[rows].cpu())
+    want = oracle_rows(ids, grad, rows, before_rows)
+    nan_g, nan_w = _is_nan_bits(got, m_dt), _is_nan_bits(want, m_dt)
+    assert np.array_equal(nan_g, nan_w), "NaN positions differ"
+    gv = got.view(np.uint16 if m_dt == "bf16" else np.uint32)
+    wv = want.view(np.uint16 if m_dt == "bf16" else np.uint32)
+    mism = (gv != wv) & ~nan_g
+    if mism.any():
+        r, c = np.argwhere(mism)[0]
+        raise AssertionError(f"{int(mism.sum())} mismatching elements; first at touched row "
+                             f"{r} (id {int(rows[r])}), column {c}: got {gv[r, c]:#x} want {wv[r, c]:#x}")
+
+    # untouched rows: bit-identical to the copy taken before the call
+    changed = (_bits(main_grad) != _bits(before)).any(dim=1)
+    touched = torch.zeros(main_grad.shape[0], dtype=torch.bool, device=main_grad.device)
+    touched[rows] = True
+    assert not (changed & ~touched).any(), "a row whose id does not occur was written"
+    return rows
+
+
+def make_case(n, vocab, hidden, grad_dtype="bf16", mg_dtype="fp32", ids=None, seed=0,
+              ids_dtype=torch.int32, shape=None):
+    rng = np.random.default_rng(seed)
+    if ids is None:
+        ids = rng.integers(0, vocab, size=n)
+    ids = torch.from_numpy(np.asarray(ids).reshape(shape or (n,))).to(ids_dtype).cuda()
+    grad = wl.normal_tensor(rng, (*ids.shape, hidden), 0.01, grad_dtype).cuda()
+    mg = wl.normal_tensor(rng, (vocab, hidden), 1e-3, mg_dtype).cuda()
+    return ids, grad, mg
+
+
+# ---- the five workloads at full size, in the launch configuration the benchmark times ----
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_full_size_bit_exact(name):
+    w = wl.WORKLOADS[name]
+    print(f"[parity] workload {name}", flush=True)
+    ids = torch.from_numpy(wl.make_ids(w)).cuda()
+    grad = wl.make_grad(w).cuda()
+    mg = wl.make_main_grad(w, "cuda")
+    rows = check_call(ids, grad, mg)
+    assert rows.numel() == np.unique(wl.make_ids(w)).size
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_sort_tables_exact(name):
+    w = wl.WORKLOADS[name]
+    ids_np = wl.make_ids(w)
+    got = ewg.sort_tokens(torch.from_numpy(ids_np).cuda(), w.vocab)
+    want = oracle.sort_tokens(ids_np)
+    for k in want:
+        assert np.array_equal(got[k].cpu().numpy().astype(np.int64), want[k]), k
+
+
+# ---- edge cases ---------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [3073, 4096, 4097, 8192])
+@pytest.mark.parametrize("hidden", [1, 7, 129, 1000])
+def test_token_counts_and_ragged_hidden(n, hidden):
+    print(f"[parity] n={n} hidden={hidden}", flush=True)
+    check_call(*make_case(n, 700, hidden, seed=n + hidden))
+
+
+@pytest.mark.parametrize("grad_dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mg_dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("hidden", [8, 1024, 7169])
+def test_dtype_pairs(grad_dtype, mg_dtype, hidden):
+    print(f"[parity] {grad_dtype}/{mg_dtype} hidden={hidden}", flush=True)
+    rng = np.random.default_rng(hidden)
+    ids = wl.zipf_ids(rng, 8192, 5000, 1.1)
+    check_call(*make_case(8192, 5000, hidden, grad_dtype, mg_dtype, ids=ids, seed=hidden))
+
+
+@pytest.mark.parametrize("hidden", [64, 1000])
+def test_all_same_id(hidden):
+    # one run of 8192 rows = 820 chunks in the ordered combine
+    check_call(*make_case(8192, 50, hidden, ids=np.full(8192, 37), seed=1))
+
+
+def test_all_distinct_ids():
+    rng = np.random.default_rng(2)
+    check_call(*make_case(8192, 20000, 300, ids=rng.permutation(20000)[:8192], seed=2))
+
+
+def test_single_row_vocabulary():
+    # num_embeddings = 1: no id bits, the sort has no pass
+    check_call(*make_case(5000, 1, 96, ids=np.zeros(5000, dtype=np.int64), seed=3))
+
+
+@pytest.mark.parametrize("n,vocab", [(8192, 1 << 18), (4096, 1 << 19)])
+def test_largest_packable_vocabulary(n, vocab):
+    # the largest ids that pack with the position into 31 bits; two 10/9-bit passes
+    rng = np.random.default_rng(4)
+    ids = rng.integers(vocab - 3000, vocab, size=n)
+    ids[:5] = vocab - 1
+    ids[5:9] = 0
+    check_call(*make_case(n, vocab, 8, ids=ids, seed=4))
+
+
+def test_int64_ids_and_2d_ids():
+    rng = np.random.default_rng(5)
+    ids = wl.zipf_ids(rng, 8192, 129280, 1.3)
+    check_call(*make_case(8192, 129280, 256, ids=ids, seed=5, ids_dtype=torch.int64,
+                          shape=(4, 2048)))
+
+
+@pytest.mark.parametrize("grad_dtype,mg_dtype", [("bf16", "fp32"), ("fp32", "bf16")])
+@pytest.mark.parametrize("pad_g,pad_m", [(8, 8), (5, 3), (0, 1)])
+def test_padded_row_strides(grad_dtype, mg_dtype, pad_g, pad_m):
+    # aligned padding keeps the 16-byte path; odd padding takes the element path
+    n, vocab, hidden = 4097, 900, 520
+    ids, grad, mg = make_case(n, vocab, hidden, grad_dtype, mg_dtype, seed=6 + pad_g)
+    gbig = torch.zeros(n, hidden + pad_g, dtype=grad.dtype, device="cuda")
+    gbig[:, :hidden] = grad
+    mbig = torch.full((vocab, hidden + pad_m), 7.0, dtype=mg.dtype, device="cuda")
+    mbig[:, :hidden] = mg
+    check_call(ids, gbig[:, :hidden], mbig[:, :hidden])
+    assert torch.all(mbig[:, hidden:] == 7.0)
+
+
+def test_special_values():
+    n, vocab, hidden = 4096, 300, 64
+    ids, grad, mg = make_case(n, vocab, hidden, "fp32", "fp32", seed=7)
+    grad[0:40] = 0.0
+    grad[40:80] = -0.0
+    grad[80:90, 3] = float("inf")
+    grad[90:95, 5] = float("-inf")
+    grad[95:99, 7] = float("nan")
+    grad[100:200] *= 1e-38                      # denormal range
+    mg[ids[40:80].long()] = -0.0
+    mg[ids[300:310].long(), 2] = float("nan")
+    check_call(ids, grad, mg)
+
+
+def test_bf16_special_values():
+    n, vocab, hidden = 4096, 300, 64
+    ids, grad, mg = make_case(n, vocab, hidden, "bf16", "bf16", seed=8)
+    grad[40:80] = -0.0
+    grad[80:90, 3] = float("inf")
+    grad[95:99, 7] = float("nan")
+    grad[100:200] *= 1e-38
+    mg[ids[40:80].long()] = -0.0
+    check_call(ids, grad, mg)
+
+
+def test_non_contiguous_grad_view():
+    n, vocab, hidden = 4096, 500, 128
+    ids, grad, mg = make_case(n, vocab, 2 * hidden, seed=9)
+    check_call(ids, grad[:, ::2], mg[:, :hidden].contiguous())
+
+
+def test_repeatable_bitwise():
+    ids, grad, mg = make_case(8192, 3000, 512, seed=10)
+    a, b = mg.clone(), mg.clone()
+    ewg.accumulate_embedding_wgrad(ids, grad, a)
+    ewg.accumulate_embedding_wgrad(ids, grad, b)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a), _bits(b))
+
+
+def test_invalid_ids_change_nothing():
+    # main_grad is an interior slice, so even a stray write would stay inside the
+    # allocation and be seen in the guard rows
+    n, vocab, hidden = 4096, 100, 32
+    ids, grad, _ = make_case(n, vocab, hidden, seed=11)
+    big = torch.randn(vocab + 2, hidden, device="cuda")
+    mg = big[1:vocab + 1]
+    before = big.clone()
+    ws = torch.empty(ewg.workspace_bytes(n, hidden), dtype=torch.uint8, device="cuda")
+    for bad in (vocab, -1):
+        ids2 = ids.clone()
+        ids2[17] = bad
+        ids2[4000] = bad
+        ewg.accumulate_embedding_wgrad(ids2, grad, mg, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(big), _bits(before))
+        assert ewg.invalid_id_count(ws) == 2
+    ewg.accumulate_embedding_wgrad(ids, grad, mg, workspace=ws)
+    torch.cuda.synchronize()
+    assert ewg.invalid_id_count(ws) == 0
+
+
+def test_sort_tables_edge_ids():
+    for ids_np, vocab in [(np.full(8192, 3), 4), (np.arange(8192)[::-1].copy(), 8192),
+                          (np.zeros(3073, dtype=np.int64), 1),
+                          (np.random.default_rng(12).integers(0, 1 << 19, 4096), 1 << 19)]:
+        got = ewg.sort_tokens(torch.from_numpy(ids_np).cuda(), vocab)
+        want = oracle.sort_tokens(ids_np)
+        for k in want:
+            assert np.array_equal(got[k].cpu().numpy().astype(np.int64), want[k]), k
