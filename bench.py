@@ -2,16 +2,17 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-One step = one whole call (sort, partial sums, long-run combine) over the
+One step = one whole call (fused sort + partial sums, long-run combine) over the
 headline workload: 8192 Zipf(1.1) token ids into a 129280 x 7168 fp32
 main_grad with a bf16 grad. Inputs are resident in HBM before timing. Before
-every step, outside its timed interval, a 1 GiB buffer is written so that
-neither L2 nor the 256 MB Infinity Cache holds the inputs. Each step is timed
+every step, outside its timed interval, a 1 GiB buffer is read (summed) so
+that neither L2 nor the 256 MB Infinity Cache holds the inputs; reading
+rather than writing leaves no dirty lines for the timed call to write back. Each step is timed
 with HIP events recorded by the library on the launch stream around each of
 its three kernels.
 
 Prints one JSON line: value = algorithmic bytes / mean call time (GB/s),
-roofline of the dominant kernel (the partial-sum pass), and the CPU oracle
+roofline of the dominant kernel (the fused sort + partial-sum kernel), and the CPU oracle
 timed on the host as cpu_baseline.
 """
 import argparse
@@ -31,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["partial_sums.hip", "ewg_device.h", "ewg_internal.h"]
+KERNEL_SOURCES = ["accumulate.hip", "sort_lds.h", "ewg_device.h", "ewg_internal.h"]
 
 
 def parse_args():
@@ -43,6 +44,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="rough budget for the CPU oracle timing")
+    p.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                   help="how the caches are emptied before each step: read (default) or write a "
+                        "1 GiB buffer, or not at all")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference for counter scaling)")
     return p.parse_args()
@@ -87,9 +91,9 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload_name):
-    """HBM bytes per launch of the partial-sum kernel from the committed counter
+    """HBM bytes per launch of the fused accumulate kernel from the committed counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"partial_sums_{workload_name}_hbm_traffic.md")
+    path = os.path.join(PROFILES, f"accumulate_{workload_name}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -152,11 +156,14 @@ def main():
     sm = 2 if w.main_grad_dtype == "bf16" else 4
     alg_bytes = wl.algorithmic_bytes(w.num_tokens, w.hidden, uniq, w.grad_dtype,
                                      w.main_grad_dtype, ids_np.itemsize)
-    # the partial-sum pass reads every grad row and updates the rows of single-chunk runs
-    ps_bytes = w.num_tokens * w.hidden * sg + 2 * u_short * w.hidden * sm
+    # the fused kernel reads the ids and every grad row and updates the rows of
+    # single-chunk runs; the long-run kernel updates the rest
+    ps_bytes = (w.num_tokens * ids_np.itemsize + w.num_tokens * w.hidden * sg
+                + 2 * u_short * w.hidden * sm)
 
-    ws = torch.empty(ewg.workspace_bytes(w.num_tokens, w.hidden), dtype=torch.uint8, device=dev)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    ws = ewg.new_workspace(w.num_tokens, w.hidden, dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     hip = HipEvents()
     nsteps = args.warmup + args.steps
     events = [hip.create(4) for _ in range(nsteps)]
@@ -171,7 +178,10 @@ def main():
         if step == args.warmup:
             torch.cuda.synchronize()
             t_wall = time.perf_counter()
-        flush.fill_(float(step))
+        if args.flush == "read":
+            flush_sink.copy_(flush.sum())
+        elif args.flush == "write":
+            flush.fill_(float(step))
         st = B.lib.accumulate_embedding_wgrad_timed(*call_args, events[step])
         if st != 0:
             raise B.EmbeddingWgradError(st, "accumulate_embedding_wgrad_timed")
@@ -179,7 +189,6 @@ def main():
     wall = time.perf_counter() - t_wall
 
     timed = events[args.warmup:]
-    t_sort = np.array([hip.ms(e[0], e[1]) for e in timed])
     t_ps = np.array([hip.ms(e[1], e[2]) for e in timed])
     t_lr = np.array([hip.ms(e[2], e[3]) for e in timed])
     t_call = np.array([hip.ms(e[0], e[3]) for e in timed])
@@ -208,8 +217,7 @@ def main():
         "ms_per_step": round(mean_call_ms, 5),
         "us_per_call": round(mean_call_ms * 1e3, 2),
         "us_per_call_p10_p50_p90": [round(float(np.percentile(t_call, q)) * 1e3, 2) for q in (10, 50, 90)],
-        "us_per_kernel": {"sort_tokens": round(float(t_sort.mean()) * 1e3, 2),
-                          "partial_sums": round(ps_ms * 1e3, 2),
+        "us_per_kernel": {"accumulate": round(ps_ms * 1e3, 2),
                           "long_run_sums": round(float(t_lr.mean()) * 1e3, 2)},
         "wall_ms_per_step_incl_cache_flush": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
@@ -221,8 +229,8 @@ def main():
                    "hidden": w.hidden, "ids": f"{w.ids_kind}" + (f"(s={w.zipf_s})" if w.ids_kind == "zipf" else ""),
                    "grad_dtype": w.grad_dtype, "main_grad_dtype": w.main_grad_dtype,
                    "distinct_ids": uniq, "runs_longer_than_10": u_long,
-                   "algorithmic_bytes": alg_bytes, "cache_flush_between_calls": True},
-        "roofline": {"bound": "hbm", "kernel": "partial_sums", "achieved": round(achieved, 1),
+                   "algorithmic_bytes": alg_bytes, "cache_flush_between_calls": args.flush},
+        "roofline": {"bound": "hbm", "kernel": "accumulate", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes_per_launch": ps_bytes,
                      "traffic": measured_traffic(name)},

@@ -119,13 +119,19 @@ size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hi
  *              in elements, each >= hidden.
  *   workspace  device scratch of at least
  *              accumulate_embedding_wgrad_workspace_bytes(num_tokens, hidden)
- *              bytes, 256-byte aligned; it must not be used by another call
- *              until this one has finished on `stream`.
+ *              bytes, 256-byte aligned, zero-filled before its first use; every
+ *              call leaves its synchronisation word zero again, so it is reused
+ *              without clearing. It must not be used by another call until this
+ *              one has finished on `stream`.
  *
- * Returns EWG_OK after enqueueing three kernels on `stream`: the LDS radix
- * sort with run marking, the partial-sum pass over the grad rows (which also
- * finishes runs of at most EWG_NROWS rows), and the ordered combine of longer
- * runs. Any alignment is accepted; 16-byte aligned rows take the vector path.
+ * Returns EWG_OK after enqueueing two kernels on `stream`: the fused kernel
+ * (one workgroup sorts the keys in LDS and publishes the chunk table while
+ * the others prefetch their share of the rows; then all sum the chunks of the
+ * grad rows, finishing runs of at most EWG_NROWS rows), and the ordered
+ * combine of longer runs. The fused kernel needs the whole device: it
+ * launches one 1024-thread workgroup per compute unit, and its workgroups
+ * wait for workgroup 0. Any alignment is accepted; 16-byte aligned rows take
+ * the vector path.
  */
 int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_grad,
                                int64_t num_tokens, int64_t hidden, int64_t num_embeddings,

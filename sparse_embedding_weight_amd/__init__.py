@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     accumulate_embedding_wgrad,
     can_accumulate_embedding_wgrad,
     invalid_id_count,
+    new_workspace,
     position_bits,
     sort_tokens,
     workspace_bytes,

@@ -119,10 +119,24 @@ def _flat_inputs(ids: torch.Tensor, grad: torch.Tensor):
     return ids_flat, grad2
 
 
+# one zero-filled workspace per (device, stream), grown on demand; calls leave
+# its flag word zero again, so it is reused without clearing
+_WORKSPACES = {}
+
+
+def new_workspace(num_tokens: int, hidden: int, device) -> torch.Tensor:
+    """A zero-filled workspace for calls with these sizes (zero-filled before first use)."""
+    return torch.zeros(workspace_bytes(num_tokens, hidden), dtype=torch.uint8, device=device)
+
+
 def _workspace(n: int, hidden: int, device, workspace):
     need = workspace_bytes(n, hidden)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        workspace = _WORKSPACES.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+            _WORKSPACES[key] = workspace
     if workspace.dtype != torch.uint8 or workspace.device != device or workspace.numel() < need:
         raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {device}")
     return workspace
@@ -135,7 +149,9 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
     ids: token ids, num_tokens elements (any shape, flattened row-major).
     grad: [*ids.shape, hidden], gradient of the lookup's output.
     main_grad: [num_embeddings, hidden], updated in place.
-    workspace: optional uint8 device tensor of >= workspace_bytes(num_tokens, hidden).
+    workspace: optional uint8 device tensor of >= workspace_bytes(num_tokens, hidden),
+        zero-filled before its first use (new_workspace() makes one); by default a
+        cached workspace per device and stream is used.
     Requires can_accumulate_embedding_wgrad(ids, grad, main_grad); raises ValueError
     otherwise. Enqueued on the current stream of main_grad's device; no sync.
     """

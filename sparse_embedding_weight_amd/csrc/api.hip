@@ -1,5 +1,5 @@
 // Host side of the C ABI declared in include/embedding_wgrad.h: argument
-// checks, workspace layout, vector-path selection and the three launches.
+// checks, workspace layout, vector-path selection and the two launches.
 // Nothing here touches device memory or synchronises; every launch goes on
 // the caller's stream.
 #include "embedding_wgrad.h"
@@ -68,6 +68,17 @@ int check_workspace(const void *workspace, size_t workspace_bytes, int64_t num_t
 
 int to_status(hipError_t e) { return e == hipSuccess ? EWG_OK : EWG_HIP_ERROR; }
 
+// A nonzero number per call: the value the fused kernel's sorting workgroup
+// publishes in the workspace's ready flag, which the combine kernel clears.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t e;
+    do {
+        e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (e == 0);
+    return e;
+}
+
 int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_tokens,
                int64_t hidden, int64_t num_embeddings, int64_t grad_row_stride,
                int64_t main_grad_row_stride, int ids_dtype, int grad_dtype, int main_grad_dtype,
@@ -94,17 +105,14 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
     const int pos_bits = ewg_position_bits(num_tokens);
     const int id_bits = bit_length((uint64_t)(num_embeddings - 1));
     const int cus = num_cus();
-    const SortTables no_tables = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
 
     (void)hipGetLastError();   // start from a clean per-thread error state
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return EWG_HIP_ERROR;
-    st = to_status(launch_sort_tokens(ids, ids_dtype == EWG_INT64, n, (int)num_embeddings, pos_bits,
-                                      id_bits, workspace, l, no_tables, stream));
-    if (st != EWG_OK) return st;
     if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
-    st = to_status(launch_partial_sums(g_bf16, m_bf16, vec2, grad, grad_row_stride, main_grad,
-                                       main_grad_row_stride, (int)hidden, workspace, l, n, cus,
-                                       stream));
+    st = to_status(launch_accumulate(ids_dtype == EWG_INT64, g_bf16, m_bf16, vec2, ids, n,
+                                     (int)num_embeddings, pos_bits, id_bits, grad, grad_row_stride,
+                                     main_grad, main_grad_row_stride, (int)hidden, workspace, l, cus,
+                                     next_epoch(), stream));
     if (st != EWG_OK) return st;
     if (events && hipEventRecord(events[2], stream) != hipSuccess) return EWG_HIP_ERROR;
     st = to_status(launch_long_run_sums(g_bf16, m_bf16, vec3, main_grad, main_grad_row_stride,

@@ -12,7 +12,8 @@
 // Work unit = (long run, column tile of 64 lanes x VEC fp32 columns); one
 // wavefront per unit, grid-stride. The adds of one column are a dependent
 // chain in chunk order, so the loads of 8 chunk sums are issued before they
-// are added.
+// are added. Block 0 also clears the fused kernel's ready flag: this kernel
+// ends every call.
 #include "ewg_device.h"
 #include "ewg_internal.h"
 
@@ -24,10 +25,12 @@ constexpr int kBatch = 8;
 
 template <typename G, typename M, int VEC>
 __global__ __launch_bounds__(kThreads) void long_run_sums_kernel(
-    const WsHeader *__restrict__ hdr, const LongRunDesc *__restrict__ runs,
+    WsHeader *__restrict__ hdr, const LongRunDesc *__restrict__ runs,
     const float *__restrict__ partial, int64_t partial_stride,
     typename M::T *__restrict__ main_grad, int64_t mg_stride, int hidden, int tiles) {
     using MT = typename M::T;
+    // the call is over for the fused kernel: clear its ready flag for the next call
+    if (blockIdx.x == 0 && threadIdx.x == 0) hdr->ready = 0u;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * kThreads + threadIdx.x) >> 6));
     const int nwaves = (int)((gridDim.x * kThreads) >> 6);
@@ -88,7 +91,7 @@ hipError_t launch(void *main_grad, int64_t mg_stride, int hidden, void *workspac
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     long_run_sums_kernel<G, M, VEC><<<(unsigned)blocks, kThreads, 0, stream>>>(
-        reinterpret_cast<const WsHeader *>(ws),
+        reinterpret_cast<WsHeader *>(ws),
         reinterpret_cast<const LongRunDesc *>(ws + l.long_runs),
         reinterpret_cast<const float *>(ws + l.partial), l.partial_stride,
         static_cast<typename M::T *>(main_grad), mg_stride, hidden, tiles);

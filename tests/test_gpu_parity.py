@@ -225,7 +225,7 @@ def test_invalid_ids_change_nothing():
     big = torch.randn(vocab + 2, hidden, device="cuda")
     mg = big[1:vocab + 1]
     before = big.clone()
-    ws = torch.empty(ewg.workspace_bytes(n, hidden), dtype=torch.uint8, device="cuda")
+    ws = ewg.new_workspace(n, hidden, "cuda")
     for bad in (vocab, -1):
         ids2 = ids.clone()
         ids2[17] = bad
