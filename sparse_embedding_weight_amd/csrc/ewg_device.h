@@ -88,6 +88,30 @@ __device__ __forceinline__ void store_vec(T *__restrict__ p, const T (&v)[N]) {
     }
 }
 
+// Pointer forms of load_vec / store_vec for a group of N elements inside a
+// larger register array.
+template <typename T, int N>
+__device__ __forceinline__ void load_piece(const T *__restrict__ p, T *out) {
+    load_vec<T, N>(p, *reinterpret_cast<T(*)[N]>(out));
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_piece(T *__restrict__ p, const T *v) {
+    store_vec<T, N>(p, *reinterpret_cast<const T(*)[N]>(v));
+}
+
+// Lane layout of a column tile of 64 lanes x VEC columns: VEC / P pieces of P
+// columns, piece s of lane l at columns s * 64 * P + l * P + [0, P) of the tile.
+// P is the largest group of at most 16 bytes in both element types, so every
+// load or store of a piece is contiguous across the wave (for bf16 grad and
+// fp32 main_grad: 8-byte grad and 16-byte main_grad pieces of 4 columns).
+template <typename G, typename M, int VEC>
+constexpr int piece_cols() {
+    constexpr int widest = sizeof(typename G::T) > sizeof(typename M::T) ? (int)sizeof(typename G::T)
+                                                                           : (int)sizeof(typename M::T);
+    return VEC < 16 / widest ? VEC : 16 / widest;
+}
+
 // Finish one element of a run: total = the ordered sum of its chunk sums.
 // Round once to grad's dtype, add to main_grad in fp32, round to its dtype.
 template <typename G, typename M>

@@ -331,27 +331,19 @@ __device__ __forceinline__ SortResult mark_runs(SortSmem &sm, int cur, int n, in
     return res;
 }
 
-// Exclusive prefix of the per-tile cost of every chunk, into out[0..n_chunks]
-// (LDS). A chunk of R rows costs R * row_cost plus end_cost_short (the
-// main_grad read and write of a single-chunk run) or end_cost_long (the store
-// of its partial sum). Returns the total. Blocked: thread t owns chunks
-// [8t, 8t + 8).
-__device__ __forceinline__ uint32_t chunk_cost_prefix(SortSmem &sm, const SortResult &res,
-                                                      uint32_t *out, uint32_t row_cost,
-                                                      uint32_t end_cost_short,
-                                                      uint32_t end_cost_long) {
+// Exclusive prefix of the per-tile cost of the chunks info[0..count), into
+// out[0..count] (LDS): a chunk of R rows costs R * row_cost + end_cost. Returns
+// the total. Blocked: thread t owns chunks [8t, 8t + 8).
+__device__ __forceinline__ uint32_t chunk_cost_prefix(SortSmem &sm, const uint32_t *info,
+                                                      int count, uint32_t *out,
+                                                      uint32_t row_cost, uint32_t end_cost) {
     const int c0 = threadIdx.x * kSortItems;
     uint32_t cost[kSortItems];
     uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const int c = c0 + j;
-        cost[j] = 0;
-        if (c < res.n_chunks) {
-            const uint32_t x = res.chunk_info[c];
-            cost[j] = (uint32_t)info_rows(x) * row_cost +
-                      ((x & kInfoLong) ? end_cost_long : end_cost_short);
-        }
+        cost[j] = c < count ? (uint32_t)info_rows(info[c]) * row_cost + end_cost : 0u;
         sum += cost[j];
     }
     uint64_t total;
@@ -359,10 +351,10 @@ __device__ __forceinline__ uint32_t chunk_cost_prefix(SortSmem &sm, const SortRe
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const int c = c0 + j;
-        if (c < res.n_chunks) out[c] = run;
+        if (c < count) out[c] = run;
         run += cost[j];
     }
-    if (threadIdx.x == 0) out[res.n_chunks] = (uint32_t)total;
+    if (threadIdx.x == 0) out[count] = (uint32_t)total;
     __syncthreads();
     return (uint32_t)total;
 }
