@@ -94,11 +94,17 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
 /*
  * Bytes of device workspace accumulate_embedding_wgrad and
  * accumulate_embedding_wgrad_sort_tokens need for these sizes (host only).
- * The workspace holds the sorted chunk tables and the fp32 partial sums of
- * runs longer than EWG_NROWS rows; its content between calls is not part of
- * the interface except for the first 4 bytes (see below). 0 if the sizes are
- * out of range.
+ * The workspace holds the chunk records and the fp32 partial sums of runs
+ * longer than EWG_NROWS rows, and the counters the kernel's workgroups share;
+ * its content between calls is not part of the interface except for two
+ * int32 words: the first 4 bytes (see below) and the one at byte offset
+ * EWG_WS_WAIT_TIMEOUTS_OFFSET, which counts the bounded waits inside the
+ * kernel that gave up since the workspace was zero-filled (a diagnostic: no
+ * wait is expected to give up; when one does, the call's result is wrong).
+ * 0 if the sizes are out of range.
  */
+#define EWG_WS_WAIT_TIMEOUTS_OFFSET 132
+
 size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);
 
 /*
@@ -124,14 +130,18 @@ size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hi
  *              without clearing. It must not be used by another call until this
  *              one has finished on `stream`.
  *
- * Returns EWG_OK after enqueueing two kernels on `stream`: the fused kernel
- * (one workgroup sorts the keys in LDS and publishes the chunk table while
- * the others prefetch their share of the rows; then all sum the chunks of the
- * grad rows, finishing runs of at most EWG_NROWS rows), and the ordered
- * combine of longer runs. The fused kernel needs the whole device: it
- * launches one 1024-thread workgroup per compute unit, and its workgroups
- * wait for workgroup 0. Any alignment is accepted; 16-byte aligned rows take
+ * Returns EWG_OK after enqueueing one kernel on `stream`. It launches one
+ * 1024-thread workgroup per compute unit. Workgroup 0 sorts the keys in LDS
+ * and publishes the chunks of runs longer than EWG_NROWS rows; meanwhile the
+ * other workgroups finish every run of at most EWG_NROWS rows; then all of
+ * them sum the chunks of the long runs and add those sums in chunk order.
+ * Workgroups hand work to each other through the workspace, and every wait in
+ * the kernel is bounded. Any alignment is accepted; 16-byte aligned rows take
  * the vector path.
+ *
+ * The workspace carries counters from one call to the next: a call that did
+ * not run to completion (for example a device fault) leaves it unusable
+ * until it is zero-filled again.
  */
 int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_grad,
                                int64_t num_tokens, int64_t hidden, int64_t num_embeddings,
@@ -140,10 +150,10 @@ int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_gra
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * accumulate_embedding_wgrad with timing markers: `events` points to 4
- * caller-created hipEvent_t, recorded on `stream` before the sort kernel,
- * before the partial-sum kernel, before the long-run kernel and after it.
- * Same arguments, results and errors otherwise; meant for benchmarks.
+ * accumulate_embedding_wgrad with timing markers: `events` points to 2
+ * caller-created hipEvent_t, recorded on `stream` right before and right
+ * after the kernel. Same arguments, results and errors otherwise; meant for
+ * benchmarks.
  */
 int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *main_grad,
                                      int64_t num_tokens, int64_t hidden, int64_t num_embeddings,

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     new_workspace,
     position_bits,
     sort_tokens,
+    wait_timeouts,
     workspace_bytes,
 )
 from ._binding import LIBRARY as library_path  # noqa: F401

@@ -202,3 +202,13 @@ def invalid_id_count(workspace: torch.Tensor) -> int:
     """Ids outside [0, num_embeddings) seen by the last call that used `workspace`
     (reads the documented first int32 of the workspace; synchronises)."""
     return int(workspace[:4].view(torch.int32).item())
+
+
+WS_WAIT_TIMEOUTS_OFFSET = 132   # EWG_WS_WAIT_TIMEOUTS_OFFSET
+
+
+def wait_timeouts(workspace: torch.Tensor) -> int:
+    """Bounded waits inside the kernel that gave up since `workspace` was
+    zero-filled (the documented diagnostic word; synchronises). Never expected."""
+    o = WS_WAIT_TIMEOUTS_OFFSET
+    return int(workspace[o:o + 4].view(torch.int32).item())

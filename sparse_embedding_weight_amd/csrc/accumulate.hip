@@ -1,39 +1,51 @@
-// Fused kernel: sort, single-chunk runs, and the chunks of long runs. One
-// 1024-thread workgroup per compute unit (at least two workgroups).
+// The whole accumulation in one kernel: sort, chunk sums, single-chunk runs
+// finished in place, and the ordered combine of long runs. One 1024-thread
+// workgroup per compute unit (at least two workgroups).
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
 // introduction's two bullets (sort the ids with their positions, sum each
 // token's rows in position order into fp32 partial sums of up to 10 rows, add
 // the partial sums in order from 0, round once to the gradient dtype, add in
-// fp32 into main_grad and round to its dtype), _sort_tokens_kernel and
-// _partial_sums_kernel ("a run of at most NROWS rows is finished here").
+// fp32 into main_grad and round to its dtype), _sort_tokens_kernel,
+// _partial_sums_kernel (a run of at most NROWS rows is finished there) and
+// _long_run_sums_kernel (the partial sums of a longer run added in order).
 //
-// The two kinds of runs need different things:
-//   * a run of at most 10 rows is one chunk. Its rows only need to be found
-//     and put in position order, which needs no global sort. Every workgroup
-//     but 0 (the "followers") builds an LDS hash table of all ids (occurrence
-//     count per id, hash slot per position), takes the runs of at most 10 rows
-//     falling in its equal-cost share of the first-occurrence order (which
-//     every follower computes identically from its own table), gathers their
-//     positions, orders them, sums the rows and finishes the main_grad row,
-//     all while workgroup 0 sorts;
-//   * a run of more than 10 rows is cut into chunks counted from its first
-//     row, which needs its rows in position order: workgroup 0 (dispatched
-//     first, so it never waits for anyone) radix-sorts the packed keys in LDS
-//     (sort_lds.h), lists the chunks of long runs with their byte cost,
-//     publishes the sorted keys and that list in the workspace with
-//     device-coherent stores, waits for them to complete and then sets the
-//     ready flag to this call's epoch (a nonzero number the host draws per
-//     call). The followers wait for the flag, copy the list into LDS with
-//     device-coherent loads (checking every entry against its bounds), and then
-//     every wave of every workgroup takes a contiguous range of (long chunk,
-//     column tile) units of about equal byte cost and stores their fp32 sums in
-//     the partial buffer. The ordered combine of those sums is the next kernel
-//     (long_run_sums.hip), which also sets the flag back to 0.
+// Phases of one launch:
+//   1. Workgroup 0 (dispatched first, it never waits for anyone) radix-sorts
+//      the packed keys in LDS (sort_lds.h) and writes, with device-coherent
+//      stores, one record per chunk of a run longer than 10 rows (its row
+//      positions and run), one per such run (main_grad row, first chunk, chunk
+//      count, first combine task). Once every store has completed it sets
+//      the ready flag to the call's epoch (a nonzero number per call).
+//   2. Meanwhile every other workgroup builds an LDS hash table of the ids
+//      and finishes its equal-cost share of the runs of at most 10 rows (a run
+//      of at most 10 rows is one chunk: it needs its rows in position order,
+//      not a global sort).
+//   3. Each wave that is done waits for the flag; then the workgroup takes
+//      batches of (long chunk, column group) units, one per wave, from a
+//      ticket counter, stores their fp32 chunk sums in the partial buffer with
+//      device-coherent stores and adds to each run's counter how many of its
+//      units the batch finished. Workgroups whose short runs took longer find
+//      fewer batches left.
+//   4. Then whole workgroups take combine tasks (one long run, one block of
+//      columns) from a ticket counter: wait until the run's units are all
+//      counted, stage its chunk sums in LDS, add them in chunk order from +0,
+//      round, add to main_grad, round.
+//   5. The last workgroup to finish clears the tickets, the exit counters and
+//      the flag for the next call. (These live in the workspace header, whose
+//      place does not depend on the sizes of a call; the per-run counters do,
+//      so workgroup 0 zeroes them before it raises the flag.)
+// Device-scope atomics on one address are serialised, so the kernel uses
+// LDS atomics for the fine-grained claims and touches every shared counter
+// about once per workgroup or batch. No wait can deadlock: the flag is raised
+// by workgroup 0, which waits for nothing before it; a combine task waits
+// only for units of batches that running workgroups have already taken, and
+// a taken batch never waits. So the launch needs no particular number of
+// resident workgroups. Every wait is bounded; a wait that gives up is counted
+// in the workspace header and its work skipped.
 //
 // A column tile is 64 lanes x VEC columns (8 for bf16 grad, 4 for fp32), laid
-// out in lane-contiguous pieces (piece_cols in ewg_device.h), and the rows of up
-// to kTilesPerUnit tiles of a chunk are loaded before the first add.
+// out in lane-contiguous pieces (piece_cols in ewg_device.h).
 #include "ewg_device.h"
 #include "ewg_internal.h"
 #include "sort_lds.h"
@@ -41,12 +53,16 @@
 namespace ewg {
 namespace {
 
-constexpr int kTilesPerUnit = 4;         // most column tiles of one chunk per batch of loads
-constexpr int64_t kWaitLimit = 1 << 22;  // polls of the ready flag before giving up (seconds)
+constexpr int kTilesPerUnit = 4;         // most column tiles of one chunk per unit / batch of loads
+constexpr int64_t kWaitLimit = 1 << 22;  // polls before a wait gives up (seconds)
 constexpr int kHashSlots = 16384;        // > 2 x kMaxTokens: linear probing always ends
 constexpr int kHashBits = 14;
 constexpr int kOwnedMax = 256;           // short runs gathered per round by one follower
 constexpr uint32_t kIdMask = (1u << 20) - 1;   // key word: id + 1 in 20 bits, round mark above
+constexpr int kStageFloats = 32768;      // combine staging: 128 KiB of chunk sums
+constexpr int kMaxCombineCols = 8192;    // columns of one combine task (8 per thread)
+constexpr int kMaxLongRuns = kMaxTokens / 11;
+constexpr int kMaxLongChunks = 2 * kMaxTokens / 11;
 
 struct FollowerSmem {
     uint32_t key[kHashSlots];               // (id + 1) | (round-local run + 1) << 20; 0 = empty
@@ -60,22 +76,35 @@ struct FollowerSmem {
     int bad;
     uint32_t first_rank;   // number of this follower's first run
     uint32_t n_mine;       // runs in this follower's share
+    uint32_t next_unit;    // next (run, tile group) unit of the round to claim
 };
 
-struct TableSmem {                          // the published long-chunk list, copied
-    uint32_t keys[kMaxTokens];
-    uint32_t info[kMaxTokens];
-    uint32_t cost[kMaxTokens + 1];
+struct CombineSmem {
+    float stage[kStageFloats];              // chunk sums of one task, [chunk][column]
+    u32x4 runs[kMaxLongRuns + 1];           // run records: row, first chunk, chunks, first task
 };
 
 union AccSmem {
     SortSmem sort;
     FollowerSmem fol;
-    TableSmem tab;
+    CombineSmem comb;
 };
 
 __device__ __forceinline__ uint32_t hash_home(uint32_t id) {
     return (id * 0x9E3779B1u) >> (32 - kHashBits);
+}
+
+// Columns of one combine task for a run of `chunks` chunk sums: the widest
+// multiple of 64 columns that lets the whole run fit the staging buffer, at
+// least 64, at most kMaxCombineCols and at most hidden rounded up to 64. Deep
+// runs get narrow tasks (many in parallel, one load round trip each), shallow
+// runs one task for all columns.
+__device__ __forceinline__ int combine_width(int chunks, int hidden) {
+    int w = kStageFloats / (chunks > 1 ? chunks : 1);
+    w = w / 64 * 64;
+    w = w < 64 ? 64 : (w > kMaxCombineCols ? kMaxCombineCols : w);
+    const int h = (hidden + 63) / 64 * 64;
+    return w < h ? w : h;
 }
 
 // NT full column tiles of one chunk of exactly R rows on the vector path,
@@ -140,11 +169,14 @@ __device__ __forceinline__ void chunk_tiles(const int32_t *pos, int row, int des
             for (int s = 0; s < S; ++s) store_piece<MT, P>(mrow + col[k][s], &out[s * P]);
         }
     } else {
-        float *prow = partial + (int64_t)dest * partial_stride;
+        // read by another workgroup in this launch: device-coherent stores
+        const __amdgpu_buffer_rsrc_t prow =
+            buffer_range(partial + (int64_t)dest * partial_stride, (uint32_t)(partial_stride * 4));
 #pragma unroll
         for (int k = 0; k < NT; ++k)
 #pragma unroll
-            for (int s = 0; s < S; ++s) store_piece<float, P>(prow + col[k][s], &acc[k][s * P]);
+            for (int s = 0; s < S; ++s)
+                store_coherent_floats<P>(prow, (uint32_t)col[k][s] * 4u, &acc[k][s * P]);
     }
 }
 
@@ -170,7 +202,8 @@ __device__ __forceinline__ void chunk_ragged_tile(const int32_t *pos, int nrows,
                 MT *m = main_grad + (int64_t)row * mg_stride + j;
                 *m = finish<G, M>(0.0f + acc, *m);
             } else {
-                partial[(int64_t)dest * partial_stride + j] = acc;
+                store_coherent(reinterpret_cast<uint32_t *>(partial + (int64_t)dest * partial_stride + j),
+                               __float_as_uint(acc));
             }
         }
 }
@@ -250,7 +283,6 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
                                                     int64_t mg_stride, int hidden, int tiles,
                                                     int me, int followers) {
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int kSlotsPerThread = kHashSlots / kSortThreads;
 
     // load the ids (all 8 loads in flight) while the table is cleared
@@ -291,7 +323,9 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             }
             h = (h + 1u) & (kHashSlots - 1);
         }
-        atomicAdd(&fs.cnt[h], 1u);
+        // counts saturate just above kNRows (only "at most 10 rows" matters), so
+        // a frequent id stops taking atomics on its slot once it is known to be long
+        if (fs.cnt[h] <= (uint32_t)kNRows) atomicAdd(&fs.cnt[h], 1u);
         fs.slot_of_pos[p] = (uint16_t)h;
         slot[i] = h;
     }
@@ -299,8 +333,9 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
     __syncthreads();
     if (fs.bad) return;   // uniform: the sorting workgroup reports it, nothing is touched
 
-    // first position per id: the high half starts at all ones, then the
-    // smallest position wins (the low half, the count, is the same for all)
+    // first position of every id of at most kNRows rows: the high half starts
+    // at all ones, then the smallest position wins (the low half, the count,
+    // is the same for all)
 #pragma unroll
     for (int k = 0; k < kSlotsPerThread; ++k) {
         const int h = k * kSortThreads + tid;
@@ -310,7 +345,11 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int p = i * kSortThreads + tid;
-        if (p < n) atomicMin(&fs.cnt[slot[i]], ((uint32_t)p << 16) | (fs.cnt[slot[i]] & 0xffffu));
+        if (p < n) {
+            const uint32_t w = fs.cnt[slot[i]];
+            if ((w & 0xffffu) <= (uint32_t)kNRows && (w >> 16) > (uint32_t)p)
+                atomicMin(&fs.cnt[slot[i]], ((uint32_t)p << 16) | (w & 0xffffu));
+        }
     }
     __syncthreads();
 
@@ -324,6 +363,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         if (tid == 0) {
             fs.first_rank = 0xffffffffu;
             fs.n_mine = 0u;
+            fs.next_unit = 0u;
         }
         // positions in blocked order: thread t owns [8t, 8t + 8); low 32 bits
         // of the scanned value = cost, high 32 bits = number of runs
@@ -387,6 +427,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         __syncthreads();
         const int n_round = total_mine - r0 < kOwnedMax ? total_mine - r0 : kOwnedMax;
         if (n_round <= 0) break;
+        const bool last_round = total_mine - r0 <= kOwnedMax;
 
         // gather the positions of the round's runs, then put each run in order
 #pragma unroll
@@ -419,9 +460,13 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         }
         __syncthreads();
 
-        // (run, group of kTilesPerUnit tiles) units over the waves
+        // (run, group of kTilesPerUnit tiles) units, claimed by the waves as they come free
         const int units = n_round * groups;
-        for (int u = wave; u < units; u += kSortWaves) {
+        for (;;) {
+            uint32_t claim = 0;
+            if ((tid & 63) == 0) claim = atomicAdd(&fs.next_unit, 1u);
+            const int u = (int)__builtin_amdgcn_readfirstlane(claim);
+            if (u >= units) break;
             const int li = u / groups, g = u - li * groups;
             const int nrows = (int)__builtin_amdgcn_readfirstlane(fs.run_len[li]);
             const int row = (int)__builtin_amdgcn_readfirstlane(fs.run_id[li]);
@@ -434,33 +479,337 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             chunk_tiles_any<G, M, VEC>(pos, nrows, row, -1, grad, grad_stride, main_grad, mg_stride,
                                        nullptr, 0, hidden, t0, t_end, full_tiles);
         }
+        // after the last round every wave goes on by itself
+        if (last_round) break;
         __syncthreads();
         if (tid < n_round) fs.key[fs.run_slot[tid]] &= kIdMask;
         __syncthreads();
-        if (total_mine - r0 <= kOwnedMax) break;
     }
 }
 
-// First unit whose start lies at or after x, in units of per-tile cost: chunk
-// c starts at cost[c] * tiles and its tiles cost cost[c+1] - cost[c] each.
-__device__ __forceinline__ void first_unit(const uint32_t *cost, int n_chunks, int tiles,
-                                           uint64_t x, int &c, int &t) {
-    const uint64_t q = x / (uint64_t)tiles;
-    int lo = 0, hi = n_chunks;   // largest c with cost[c] <= q, in [0, n_chunks)
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((uint64_t)__builtin_amdgcn_readfirstlane(cost[mid]) <= q) lo = mid; else hi = mid;
-    }
-    c = lo;
-    const uint64_t start = (uint64_t)__builtin_amdgcn_readfirstlane(cost[c]) * (uint64_t)tiles;
-    const uint64_t per_tile = (uint64_t)(__builtin_amdgcn_readfirstlane(cost[c + 1]) -
-                                         __builtin_amdgcn_readfirstlane(cost[c]));
-    const uint64_t tt = (x - start + per_tile - 1) / per_tile;   // first tile starting at or after x
-    if (tt >= (uint64_t)tiles) {
-        ++c;
-        t = 0;
+
+// ---- phase 1: the sorting workgroup -------------------------------------------
+
+// Sort, mark runs, write the unit and run records, zero the runs' unit counts
+// and the tickets, publish the counts and raise the flag. With an id out of
+// range there is nothing to do: all counts are 0.
+template <typename IdT>
+__device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restrict__ ids, int n,
+                                               int num_embeddings, int pos_bits, int id_bits,
+                                               int hidden, WsHeader *__restrict__ hdr,
+                                               __amdgpu_buffer_rsrc_t units_rs,
+                                               __amdgpu_buffer_rsrc_t runs_rs,
+                                               uint32_t *__restrict__ done, uint32_t epoch) {
+    const int tid = threadIdx.x;
+    uint32_t n_lc = 0, n_lr = 0, n_tasks = 0;
+    const SortOutputs out0 = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
+                              nullptr, nullptr};
+    const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits);
+    if (bad) {
+        report_invalid(out0, bad);
     } else {
-        t = (int)tt;
+        const int cur = radix_sort_ids(ss, pos_bits, id_bits);
+        // after the sort, aux holds: the run of every long chunk, the long-run
+        // list (4 words each) and the chunk word of every long chunk
+        uint32_t *lc_run = ss.aux;
+        uint32_t *lr = ss.aux + 2048;
+        uint32_t *lc_info = ss.aux + 8192;
+        static_assert(kMaxLongChunks <= 2048 && 2048 + 4 * kMaxLongRuns <= 8192 &&
+                          8192 + kMaxLongChunks <= (kSortWaves << kMaxDigitBits),
+                      "long-run tables fit the sort's counter space");
+        const SortOutputs out = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
+                                 lc_run, lr};
+        const SortResult res = mark_runs(ss, cur, n, pos_bits, out);
+        for (int c = tid; c < res.n_chunks; c += kSortThreads) {
+            const uint32_t x = res.chunk_info[c];
+            if (x & kInfoLong) lc_info[info_long_chunk(x)] = x;
+        }
+        __syncthreads();
+        n_lc = (uint32_t)res.n_long_chunks;
+        n_lr = (uint32_t)res.n_long;
+
+        // unit records: positions of the chunk's rows (16 bits each), rows | run << 16,
+        // chunk number, epoch
+        const uint32_t pos_mask = (1u << pos_bits) - 1u;
+        for (int c = tid; c < (int)n_lc; c += kSortThreads) {
+            const uint32_t x = lc_info[c];
+            const int f = info_first(x), rows = info_rows(x);
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const uint32_t a = 2 * i < rows ? res.keys[f + 2 * i] & pos_mask : 0u;
+                const uint32_t b = 2 * i + 1 < rows ? res.keys[f + 2 * i + 1] & pos_mask : 0u;
+                w[i] = a | (b << 16);
+            }
+            w[5] = (uint32_t)rows | (lc_run[c] << 16);
+            w[6] = (uint32_t)c;
+            w[7] = epoch;
+            store_coherent16(units_rs, (uint32_t)c * kUnitRecordBytes, u32x4{w[0], w[1], w[2], w[3]});
+            store_coherent16(units_rs, (uint32_t)c * kUnitRecordBytes + 16, u32x4{w[4], w[5], w[6], w[7]});
+        }
+        // run records, with the exclusive prefix of their combine tasks; unit counts to 0
+        uint32_t tasks = 0, chunks = 0;
+        if (tid < (int)n_lr) {
+            chunks = lr[4 * tid + 2];
+            const uint32_t wdt = (uint32_t)combine_width((int)chunks, hidden);
+            tasks = ((uint32_t)hidden + wdt - 1) / wdt;
+        }
+        uint64_t total;
+        const uint32_t first_task = (uint32_t)block_exclusive_scan(tasks, ss.scan, &total);
+        if (tid < (int)n_lr) {
+            store_coherent16(runs_rs, (uint32_t)tid * kRunRecordBytes,
+                             u32x4{lr[4 * tid], lr[4 * tid + 1], chunks, first_task});
+            store_coherent(&done[tid * kDoneStride], 0u);
+        }
+        n_tasks = (uint32_t)total;
+
+    }
+    if (tid == 0) {
+        store_coherent(&hdr->pub_long_chunks, n_lc);
+        store_coherent(&hdr->pub_long_runs, n_lr);
+        store_coherent(&hdr->pub_tasks, n_tasks);
+        store_coherent(&hdr->unit_ticket, 0u);
+        store_coherent(&hdr->task_ticket, 0u);
+    }
+    // every store of every wave has completed, then the flag goes up
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) store_coherent(&hdr->ready, epoch);
+}
+
+// ---- phase 3: chunks of long runs ---------------------------------------------
+
+// Wave-level wait for this call's flag; false if the wait gave up.
+__device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint32_t epoch) {
+    int64_t spins = 0;
+    while (__builtin_amdgcn_readfirstlane(load_coherent(&hdr->ready)) != epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kWaitLimit) {
+            if ((threadIdx.x & 63) == 0) fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+            return false;
+        }
+    }
+    return true;
+}
+
+// Long units (chunk c, column tile k) = c * tiles + k, handed out in batches
+// of one unit per wave: thread 0 takes batches from the device-wide ticket
+// (one serialised atomic per batch; the next batch is taken while the
+// current one runs), each wave does one unit of the batch, storing the chunk
+// sums of its columns in partial row c with device-coherent stores, and once
+// all have completed the batch's units are counted for their runs (a batch is
+// contiguous, so units of one run are adjacent: one atomic per run of the
+// batch). Workgroups that come late find the tickets gone, which evens out
+// the end of the short-run phase; single-tile units keep the last batches
+// short.
+template <typename G, typename M, int VEC>
+__device__ __forceinline__ void long_units(uint32_t *s_word, uint32_t *s_run,
+                                           WsHeader *__restrict__ hdr,
+                                           __amdgpu_buffer_rsrc_t units_rs,
+                                           uint32_t *__restrict__ done, uint32_t total,
+                                           uint32_t n_lr, int n,
+                                           const typename G::T *__restrict__ grad,
+                                           int64_t grad_stride, float *__restrict__ partial,
+                                           int64_t partial_stride, int hidden, int tiles,
+                                           uint32_t epoch) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int full_tiles = hidden / (64 * VEC);
+    constexpr uint32_t kBatch = kSortWaves;
+    // batch numbers alternate between two LDS words: the one written during a
+    // batch is read after its closing barrier, and rewritten only a batch later
+    if (tid == 0) {
+        uint32_t b = load_coherent(&hdr->unit_ticket);   // a plain look first
+        if (b < total) b = fetch_add_coherent(&hdr->unit_ticket, kBatch);
+        s_word[2] = b;
+    }
+    __syncthreads();
+    uint32_t b = s_word[2];
+    for (int k = 1; b < total; ++k) {   // uniform
+        uint32_t next = 0;
+        if (tid == 0) next = fetch_add_coherent(&hdr->unit_ticket, kBatch);
+        const uint32_t t = b + (uint32_t)wave;
+        uint32_t run = 0xffffffffu;
+        if (t < total) {
+            const uint32_t c = t / (uint32_t)tiles;
+            const int tile = (int)(t - c * (uint32_t)tiles);
+            const u32x4 ra = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes);
+            const u32x4 rb = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes + 16);
+            uint32_t w[6] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y};
+#pragma unroll
+            for (int i = 0; i < 6; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+            int rows = (int)(w[5] & 0xffffu);
+            rows = rows < 1 ? 1 : (rows > kNRows ? kNRows : rows);
+            int32_t pos[kNRows];
+#pragma unroll
+            for (int r = 0; r < kNRows; ++r) {
+                const uint32_t q = (w[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+                pos[r] = q < (uint32_t)n ? (int32_t)q : 0;   // every row inside grad
+            }
+            // a record of another call (never expected) is counted and its unit skipped
+            if (__builtin_amdgcn_readfirstlane(rb.w) == epoch) {
+                chunk_tiles_any<G, M, VEC>(pos, rows, 0, (int)c, grad, grad_stride, nullptr, 0,
+                                           partial, partial_stride, hidden, tile, tile + 1,
+                                           full_tiles);
+                run = w[5] >> 16;
+            } else if ((tid & 63) == 0) {
+                fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+            }
+        }
+        // runs of the batch's units, in the buffer of this batch's parity: a wave
+        // without a unit in the next batch writes at once, while wave 0 may
+        // still be counting this one
+        uint32_t *runs_k = s_run + (k & 1) * kSortWaves;
+        if ((tid & 63) == 0) runs_k[wave] = run;
+        if (tid == 0) s_word[2 + (k & 1)] = next;
+        // the chunk sums of every wave have completed before they are counted
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid < kSortWaves) {
+            const uint32_t r = runs_k[tid];
+            if (r < n_lr && (tid == 0 || runs_k[tid - 1] != r)) {
+                uint32_t m = 1;
+                while (tid + (int)m < kSortWaves && runs_k[tid + m] == r) ++m;
+                fetch_add_coherent(&done[r * kDoneStride], m);
+            }
+        }
+        b = s_word[2 + (k & 1)];
+    }
+}
+
+// ---- phase 4: ordered combine of long runs -------------------------------------
+
+template <typename G, typename M>
+__device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
+                                              WsHeader *__restrict__ hdr,
+                                              __amdgpu_buffer_rsrc_t runs_rs,
+                                              uint32_t *__restrict__ done,
+                                              const float *__restrict__ partial,
+                                              int64_t partial_stride,
+                                              typename M::T *__restrict__ main_grad,
+                                              int64_t mg_stride, int hidden, int tiles,
+                                              int num_embeddings, uint32_t n_lc_max,
+                                              uint32_t n_lr_max) {
+    using MT = typename M::T;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        const uint32_t lr = load_coherent(&hdr->pub_long_runs);
+        s_word[0] = lr < n_lr_max ? lr : n_lr_max;
+        s_word[1] = load_coherent(&hdr->pub_tasks);
+    }
+    __syncthreads();
+    const int n_lr = (int)s_word[0];
+    const uint32_t n_tasks = s_word[1];
+    if (n_lr == 0 || n_tasks == 0) return;   // uniform
+    for (int r = tid; r < n_lr; r += kSortThreads) cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
+    __syncthreads();
+
+    for (;;) {
+        if (tid == 0) {
+            // a cheap look first: most late workgroups find the tasks gone
+            // without a serialised atomic
+            uint32_t t = load_coherent(&hdr->task_ticket);
+            if (t < n_tasks) t = fetch_add_coherent(&hdr->task_ticket, 1u);
+            s_word[2] = t;
+        }
+        __syncthreads();
+        const uint32_t t = s_word[2];
+        if (t >= n_tasks) break;   // uniform
+        // the run: the last one whose first task is at or before t
+        int lo = 0, hi = n_lr;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cs.runs[mid].w <= t) lo = mid; else hi = mid;
+        }
+        const u32x4 rec = cs.runs[lo];
+        const uint32_t row = rec.x, first = rec.y, chunks = rec.z;
+        const int wdt = combine_width((int)chunks, hidden);
+        const int64_t col0 = (int64_t)(t - rec.w) * wdt;
+        // a record that does not describe this call's work is skipped
+        const bool valid = rec.w <= t && row < (uint32_t)num_embeddings && chunks >= 1 &&
+                           first < n_lc_max && chunks <= n_lc_max - first && col0 < hidden;
+        if (tid == 0) {
+            int ok = valid ? 1 : 0;
+            const uint32_t target = chunks * (uint32_t)tiles;
+            int64_t spins = 0;
+            while (ok && load_coherent(&done[lo * kDoneStride]) < target) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kWaitLimit) {
+                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+                    ok = 0;
+                }
+            }
+            s_word[3] = (uint32_t)ok;
+        }
+        __syncthreads();
+        if (s_word[3]) {   // uniform
+            const int wc = (int)(hidden - col0 < wdt ? hidden - col0 : wdt);
+            MT *mrow = main_grad + (int64_t)row * mg_stride + col0;
+            constexpr int kCols = kMaxCombineCols / kSortThreads;   // columns per thread
+            MT old[kCols];
+            float total[kCols];
+#pragma unroll
+            for (int i = 0; i < kCols; ++i) {
+                const int j = tid + i * kSortThreads;
+                total[i] = 0.0f;
+                if (j < wc) old[i] = mrow[j];
+            }
+            const int quads = (wc + 3) / 4;           // 16-byte pieces of one chunk row
+            // chunks per stage: the buffer, and a byte range below 2 GiB
+            int per_stage = kStageFloats / wdt;
+            const int64_t by_range = ((int64_t)1 << 29) / partial_stride;
+            if (per_stage > by_range) per_stage = (int)by_range;
+            for (int k0 = 0; k0 < (int)chunks; k0 += per_stage) {
+                const int ks = (int)chunks - k0 < per_stage ? (int)chunks - k0 : per_stage;
+                const float *base = partial + (int64_t)(first + k0) * partial_stride + col0;
+                const uint32_t range = (uint32_t)(((int64_t)(ks - 1) * partial_stride + 4 * quads) * 4);
+                const __amdgpu_buffer_rsrc_t rs = buffer_range(base, range);
+                const int pieces = ks * quads;
+                constexpr int kLoads = kStageFloats / 4 / kSortThreads;
+                u32x4 v[kLoads];
+#pragma unroll
+                for (int i = 0; i < kLoads; ++i) {   // all loads in flight; past the range they read 0
+                    const int p = tid + i * kSortThreads;
+                    const int kk = p / quads, q = p - kk * quads;
+                    const uint32_t off = p < pieces ? (uint32_t)(((int64_t)kk * partial_stride + 4 * q) * 4)
+                                                    : 0xfffffff0u;
+                    v[i] = load_coherent16(rs, off);
+                }
+#pragma unroll
+                for (int i = 0; i < kLoads; ++i) {
+                    const int p = tid + i * kSortThreads;
+                    if (p < pieces) {
+                        const int kk = p / quads, q = p - kk * quads;
+                        float *d = &cs.stage[kk * wdt + 4 * q];
+                        d[0] = __uint_as_float(v[i].x);
+                        d[1] = __uint_as_float(v[i].y);
+                        d[2] = __uint_as_float(v[i].z);
+                        d[3] = __uint_as_float(v[i].w);
+                    }
+                }
+                __syncthreads();
+                // in chunk order, one running total per column; waves without
+                // a column of this slot skip it
+#pragma unroll
+                for (int i = 0; i < kCols; ++i) {
+                    const int wave_j0 = (tid & ~63) + i * kSortThreads;
+                    if (wave_j0 < wc) {
+                        const int j = tid + i * kSortThreads;
+                        const float *col = &cs.stage[j < wc ? j : wave_j0];
+                        float acc = total[i];
+                        for (int kk = 0; kk < ks; ++kk) acc = acc + col[kk * wdt];
+                        total[i] = acc;
+                    }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < kCols; ++i) {
+                const int j = tid + i * kSortThreads;
+                if (j < wc) mrow[j] = finish<G, M>(total[i], old[i]);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -468,169 +817,61 @@ template <typename IdT, typename G, typename M, int VEC>
 __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     const IdT *__restrict__ ids, int n, int num_embeddings, int pos_bits, int id_bits,
     const typename G::T *__restrict__ grad, int64_t grad_stride,
-    typename M::T *__restrict__ main_grad, int64_t mg_stride, float *__restrict__ partial,
-    int64_t partial_stride, int hidden, int tiles, WsHeader *__restrict__ hdr,
-    uint32_t *__restrict__ tab_keys, uint32_t *__restrict__ tab_info,
-    uint32_t *__restrict__ tab_cost, LongRunDesc *__restrict__ long_runs, uint32_t epoch) {
+    typename M::T *__restrict__ main_grad, int64_t mg_stride, int hidden, int tiles,
+    WsHeader *__restrict__ hdr, uint8_t *__restrict__ units,
+    uint8_t *__restrict__ runs, uint32_t *__restrict__ done, float *__restrict__ partial,
+    int64_t partial_stride, uint32_t epoch) {
     __shared__ AccSmem sm;
-    __shared__ int s_flag;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
+    __shared__ uint32_t s_run[2 * kSortWaves];
+    const int tid = threadIdx.x;
+    const uint32_t n_lc_max = (uint32_t)(2 * n / 11), n_lr_max = (uint32_t)(n / 11);
+    const __amdgpu_buffer_rsrc_t units_rs = buffer_range(units, n_lc_max * (uint32_t)kUnitRecordBytes);
+    const __amdgpu_buffer_rsrc_t runs_rs = buffer_range(runs, n_lr_max * (uint32_t)kRunRecordBytes);
+    if (tid == 0) s_word[0] = 0u;   // set by waves that gave up on the flag; read after barriers
 
-    const uint32_t *keys, *info, *cost;
-    int n_lc;              // chunks of long runs
-    uint32_t cost_total;   // their summed per-tile cost
+    bool ready = true;
     if (blockIdx.x == 0) {
-        // ---- the sorting workgroup ----
-        SortSmem &ss = sm.sort;
-        const SortOutputs out = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr},
-                                 long_runs, hdr};
-        const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits);
-        if (bad) {
-            report_invalid(out, bad);
-            n_lc = 0;
-            cost_total = 0;
-            keys = info = cost = nullptr;
-        } else {
-            const int cur = radix_sort_ids(ss, pos_bits, id_bits);
-            const SortResult res = mark_runs(ss, cur, n, pos_bits, out);
-            // the long chunks in order: a long chunk's index is stored in its word
-            uint32_t *lc_info = ss.aux;
-            uint32_t *lc_cost = ss.aux + kMaxTokens;
-            for (int c = tid; c < res.n_chunks; c += kSortThreads) {
-                const uint32_t x = res.chunk_info[c];
-                if (x & kInfoLong) lc_info[info_long_chunk(x)] = x;
-            }
-            __syncthreads();
-            n_lc = res.n_long_chunks;
-            // per-tile cost in 16-byte lane loads: the grad rows and the partial store
-            const uint32_t row_cost = (uint32_t)(VEC * sizeof(typename G::T) + 15) / 16;
-            const uint32_t end_cost = (uint32_t)(VEC * 4 + 15) / 16;
-            cost_total = chunk_cost_prefix(ss, lc_info, n_lc, lc_cost, row_cost, end_cost);
-            keys = res.keys;
-            info = lc_info;
-            cost = lc_cost;
-            // device-coherent stores: they reach the coherence point, no L2 write-back
-            for (int i = tid; i < n; i += kSortThreads)
-                __hip_atomic_store(&tab_keys[i], keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int i = tid; i < n_lc; i += kSortThreads)
-                __hip_atomic_store(&tab_info[i], info[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int i = tid; i <= n_lc; i += kSortThreads)
-                __hip_atomic_store(&tab_cost[i], cost[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (tid == 0) {
-            __hip_atomic_store(&hdr->num_long_chunks, n_lc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->cost_total, cost_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // every store of every wave has completed, then the flag goes up
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&hdr->ready, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        leader_publish<IdT>(sm.sort, ids, n, num_embeddings, pos_bits, id_bits, hidden, hdr,
+                            units_rs, runs_rs, done, epoch);
     } else {
-        // ---- the followers: short runs, then wait for the long-chunk list ----
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, grad, grad_stride,
                                             main_grad, mg_stride, hidden, tiles,
                                             (int)blockIdx.x - 1, (int)gridDim.x - 1);
-        if (tid == 0) {
-            int ok = 1;
-            int64_t spins = 0;
-            while (__hip_atomic_load(&hdr->ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kWaitLimit) {
-                    atomicAdd(&hdr->wait_timeouts, 1);
-                    ok = 0;
-                    break;
-                }
-            }
-            s_flag = ok;
-        }
-        __syncthreads();
-        if (!s_flag) return;   // uniform; never expected
-        n_lc = __hip_atomic_load(&hdr->num_long_chunks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        cost_total = __hip_atomic_load(&hdr->cost_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the list must be in bounds whatever was read: clamp the count
-        const int max_lc = 2 * n / 11;
-        n_lc = n_lc < 0 ? 0 : (n_lc > max_lc ? max_lc : n_lc);
-        if (n_lc > 0) {
-            // one round trip: every load of the copy is issued before the first store
-            TableSmem &tb = sm.tab;
-            uint32_t kv[kSortItems], iv[2], cv[2];
-#pragma unroll
-            for (int i = 0; i < kSortItems; ++i) {
-                const int j = i * kSortThreads + tid;
-                kv[i] = __hip_atomic_load(&tab_keys[j < n ? j : n - 1], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int j = i * kSortThreads + tid;
-                iv[i] = __hip_atomic_load(&tab_info[j < n_lc ? j : n_lc - 1], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-                cv[i] = __hip_atomic_load(&tab_cost[j <= n_lc ? j : n_lc], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-            }
-            const uint32_t pos_mask = (1u << pos_bits) - 1u;
-#pragma unroll
-            for (int i = 0; i < kSortItems; ++i) {
-                const int j = i * kSortThreads + tid;
-                // keep every position below n
-                if (j < n) tb.keys[j] = (kv[i] & pos_mask) < (uint32_t)n ? kv[i] : (kv[i] & ~pos_mask);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int j = i * kSortThreads + tid;
-                if (j < n_lc) {
-                    // first slot and rows inside [0, n), chunk index inside the list
-                    uint32_t x = iv[i];
-                    const int f = info_first(x), r = info_rows(x);
-                    if (f + r > n || info_long_chunk(x) >= max_lc) x = (uint32_t)j << 17;   // 1 row at slot 0
-                    tb.info[j] = x;
-                }
-                if (j <= n_lc) tb.cost[j] = cv[i];
-            }
-            __syncthreads();
-            // costs must increase for the range search: one wave checks
-            if (wave == 0) {
-                bool ok = true;
-                for (int j = tid; j < n_lc; j += 64) ok = ok && tb.cost[j] < tb.cost[j + 1];
-                if (!__all(ok)) {
-                    for (int j = tid; j <= n_lc; j += 64) tb.cost[j] = (uint32_t)j;
-                    if (tid == 0) cost_total = (uint32_t)n_lc;
-                }
-            }
-            __syncthreads();
-            cost_total = tb.cost[n_lc];
-        }
-        keys = sm.tab.keys;
-        info = sm.tab.info;
-        cost = sm.tab.cost;
+        ready = wave_wait_ready(hdr, epoch);
     }
-    if (n_lc == 0) return;
+    // all waves of the workgroup are past their short runs and the flag
+    if (!ready && (tid & 63) == 0) atomicOr(&s_word[0], 1u);
+    __syncthreads();
+    if (s_word[0] == 0u) {   // uniform: every wave saw the flag
+        const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
+        const uint32_t n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
+        long_units<G, M, VEC>(s_word, s_run, hdr, units_rs, done, n_lc * (uint32_t)tiles, n_lr, n,
+                              grad, grad_stride, partial, partial_stride, hidden, tiles, epoch);
+    }
+    __syncthreads();
+    combine_tasks<G, M>(sm.comb, s_word, hdr, runs_rs, done, partial, partial_stride, main_grad,
+                        mg_stride, hidden, tiles, num_embeddings, n_lc_max, n_lr_max);
 
-    // ---- long chunks: this wave's units start in [x0, x1) of the cost line ----
-    const uint32_t pos_mask = (1u << pos_bits) - 1u;
-    const uint64_t nw = (uint64_t)gridDim.x * kSortWaves;
-    const uint64_t gw = (uint64_t)blockIdx.x * kSortWaves + (uint64_t)__builtin_amdgcn_readfirstlane(wave);
-    const uint64_t total = (uint64_t)cost_total * (uint64_t)tiles;
-    int c, t, ce, te;
-    first_unit(cost, n_lc, tiles, total * gw / nw, c, t);
-    if (gw + 1 == nw) {
-        ce = n_lc;
-        te = 0;
-    } else {
-        first_unit(cost, n_lc, tiles, total * (gw + 1) / nw, ce, te);
-    }
-    const int full_tiles = hidden / (64 * VEC);
-    for (; c < ce || (c == ce && t < te); ++c, t = 0) {
-        const uint32_t x = __builtin_amdgcn_readfirstlane(info[c]);
-        const int f = info_first(x), nrows = info_rows(x);
-        const int dest = info_long_chunk(x);
-        int32_t pos[kNRows];
-#pragma unroll
-        for (int r = 0; r < kNRows; ++r)
-            pos[r] = r < nrows ? (int32_t)(__builtin_amdgcn_readfirstlane(keys[f + r]) & pos_mask) : 0;
-        const int t_stop = c == ce ? te : tiles;
-        chunk_tiles_any<G, M, VEC>(pos, nrows, 0, dest, grad, grad_stride, main_grad, mg_stride,
-                                   partial, partial_stride, hidden, t, t_stop, full_tiles);
+    // ---- phase 5: the last workgroup out resets the call's shared state ----
+    // two levels of counters, so that no address takes more than ~32 atomics
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t grp = blockIdx.x % kExitGroups;
+        const uint32_t members = (gridDim.x - grp + kExitGroups - 1) / kExitGroups;
+        uint32_t last = 0;
+        if (fetch_add_coherent(&hdr->exit_group[grp][0], 1u) == members - 1) {
+            const uint32_t used = gridDim.x < kExitGroups ? gridDim.x : kExitGroups;
+            last = fetch_add_coherent(&hdr->exit_top, 1u) == used - 1 ? 1u : 0u;
+        }
+        if (last) {
+            for (int g = 0; g < kExitGroups; ++g) store_coherent(&hdr->exit_group[g][0], 0u);
+            store_coherent(&hdr->exit_top, 0u);
+            store_coherent(&hdr->unit_ticket, 0u);
+            store_coherent(&hdr->task_ticket, 0u);
+            store_coherent(&hdr->ready, 0u);
+        }
     }
 }
 
@@ -641,16 +882,14 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int pos_bits, int 
                   hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     const int tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
-    // at least one follower; workgroup 0 never waits, so any residency works
-    const int grid = num_cus > 2 ? num_cus : 2;
+    const int grid = num_cus < 2 ? 2 : (num_cus > kMaxGrid ? kMaxGrid : num_cus);
     accumulate_kernel<IdT, G, M, VEC><<<grid, kSortThreads, 0, stream>>>(
         static_cast<const IdT *>(ids), n, num_embeddings, pos_bits, id_bits,
         static_cast<const typename G::T *>(grad), grad_stride,
-        static_cast<typename M::T *>(main_grad), mg_stride,
-        reinterpret_cast<float *>(ws + l.partial), l.partial_stride, hidden, tiles,
-        reinterpret_cast<WsHeader *>(ws), reinterpret_cast<uint32_t *>(ws + l.keys),
-        reinterpret_cast<uint32_t *>(ws + l.info), reinterpret_cast<uint32_t *>(ws + l.cost),
-        reinterpret_cast<LongRunDesc *>(ws + l.long_runs), epoch);
+        static_cast<typename M::T *>(main_grad), mg_stride, hidden, tiles,
+        reinterpret_cast<WsHeader *>(ws), reinterpret_cast<uint8_t *>(ws + l.units), reinterpret_cast<uint8_t *>(ws + l.runs),
+        reinterpret_cast<uint32_t *>(ws + l.done), reinterpret_cast<float *>(ws + l.partial),
+        l.partial_stride, epoch);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Host side of the C ABI declared in include/embedding_wgrad.h: argument
-// checks, workspace layout, vector-path selection and the two launches.
+// checks, workspace layout, vector-path selection and the launch.
 // Nothing here touches device memory or synchronises; every launch goes on
 // the caller's stream.
 #include "embedding_wgrad.h"
@@ -68,8 +68,8 @@ int check_workspace(const void *workspace, size_t workspace_bytes, int64_t num_t
 
 int to_status(hipError_t e) { return e == hipSuccess ? EWG_OK : EWG_HIP_ERROR; }
 
-// A nonzero number per call: the value the fused kernel's sorting workgroup
-// publishes in the workspace's ready flag, which the combine kernel clears.
+// A nonzero number per call: the value the kernel's sorting workgroup
+// publishes in the workspace's ready flag, which its last workgroup clears.
 uint32_t next_epoch() {
     static std::atomic<uint32_t> counter{0};
     uint32_t e;
@@ -92,33 +92,25 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
 
     const bool g_bf16 = grad_dtype == EWG_BF16, m_bf16 = main_grad_dtype == EWG_BF16;
     const size_t gs = float_size(grad_dtype), ms = float_size(main_grad_dtype);
-    // partial-sum kernel: a lane moves 16 bytes of grad and the same columns of main_grad
+    // vector path: a lane moves 16 bytes of grad and the same columns of main_grad
     const int vec_g = (int)(16 / gs);
-    const bool vec2 = aligned(grad, grad_row_stride * (int64_t)gs, 16) &&
-                      aligned(main_grad, main_grad_row_stride * (int64_t)ms,
-                              vec_g * ms < 16 ? vec_g * ms : 16);
-    // long-run kernel: a lane moves 4 fp32 partial sums and 4 main_grad columns
-    const bool vec3 = aligned(main_grad, main_grad_row_stride * (int64_t)ms, 4 * ms < 16 ? 4 * ms : 16);
+    const bool vec = aligned(grad, grad_row_stride * (int64_t)gs, 16) &&
+                     aligned(main_grad, main_grad_row_stride * (int64_t)ms,
+                             vec_g * ms < 16 ? vec_g * ms : 16);
 
     const WsLayout l = ws_layout(num_tokens, hidden);
     const int n = (int)num_tokens;
     const int pos_bits = ewg_position_bits(num_tokens);
     const int id_bits = bit_length((uint64_t)(num_embeddings - 1));
-    const int cus = num_cus();
 
     (void)hipGetLastError();   // start from a clean per-thread error state
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return EWG_HIP_ERROR;
-    if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
-    st = to_status(launch_accumulate(ids_dtype == EWG_INT64, g_bf16, m_bf16, vec2, ids, n,
+    st = to_status(launch_accumulate(ids_dtype == EWG_INT64, g_bf16, m_bf16, vec, ids, n,
                                      (int)num_embeddings, pos_bits, id_bits, grad, grad_row_stride,
-                                     main_grad, main_grad_row_stride, (int)hidden, workspace, l, cus,
-                                     next_epoch(), stream));
+                                     main_grad, main_grad_row_stride, (int)hidden, workspace, l,
+                                     num_cus(), next_epoch(), stream));
     if (st != EWG_OK) return st;
-    if (events && hipEventRecord(events[2], stream) != hipSuccess) return EWG_HIP_ERROR;
-    st = to_status(launch_long_run_sums(g_bf16, m_bf16, vec3, main_grad, main_grad_row_stride,
-                                        (int)hidden, workspace, l, n / 11, cus, stream));
-    if (st != EWG_OK) return st;
-    if (events && hipEventRecord(events[3], stream) != hipSuccess) return EWG_HIP_ERROR;
+    if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
     return EWG_OK;
 }
 

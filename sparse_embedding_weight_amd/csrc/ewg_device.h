@@ -112,6 +112,67 @@ constexpr int piece_cols() {
     return VEC < 16 / widest ? VEC : 16 / widest;
 }
 
+// ---- device-coherent moves -------------------------------------------------
+// Data that one workgroup writes and another reads in the same launch (the
+// partial sums of long runs, the chunk and run records) bypasses the
+// non-coherent part of the cache hierarchy: 32-bit loads and stores go through
+// relaxed device-scope atomics; wider ones use raw buffer instructions with the
+// same device-scope cache policy. A buffer instruction also checks its offset
+// against the byte range of its resource: an access past the range reads 0
+// and writes nothing.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;   // untyped 32-bit elements, no swizzle
+constexpr int kDeviceScope = 16;              // cache-policy bits of device scope
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRawBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kDeviceScope);
+}
+
+__device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                 u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kDeviceScope);
+}
+
+// P consecutive floats (P = 1, 2 or a multiple of 4), aligned to
+// min(16, 4 * P) bytes.
+template <int P>
+__device__ __forceinline__ void store_coherent_floats(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                      const float *v) {
+    if constexpr (P % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < P / 4; ++k) {
+            const u32x4 w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                             __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(byte_off + 16u * k), 0, kDeviceScope);
+        }
+    } else if constexpr (P == 2) {
+        const u32x2 w = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)byte_off, 0, kDeviceScope);
+    } else {
+        static_assert(P == 1, "pieces of 1, 2 or 4k floats");
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, (int)byte_off, 0,
+                                              kDeviceScope);
+    }
+}
+
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t fetch_add_coherent(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Finish one element of a run: total = the ordered sum of its chunk sums.
 // Round once to grad's dtype, add to main_grad in fp32, round to its dtype.
 template <typename G, typename M>

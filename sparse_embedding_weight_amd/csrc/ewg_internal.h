@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "embedding_wgrad.h"
+
 namespace ewg {
 
 constexpr int kNRows = 10;           // rows per partial sum (NROWS_PER_THREAD)
@@ -15,33 +17,45 @@ constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortItems = kMaxTokens / kSortThreads;   // keys per thread
 constexpr int kMaxDigitBits = 10;    // radix digit of one sort pass
 
-// Workspace header, at offset 0. invalid_ids is the documented first int32.
+// Workspace header, at offset 0: eight 128-byte cache lines. invalid_ids is
+// the documented first int32. Line 0 is written with plain stores by the sort
+// step and read only by the host; the other lines are only accessed with
+// device-coherent loads, stores and atomics. Device-scope atomics on one
+// address are serialised (about 11 ns each on MI355X), so every counter that
+// many workgroups update has a line of its own and is touched once per
+// workgroup, not once per wave.
+constexpr int kExitGroups = 8;       // exit counters: one per group of workgroups (XCD)
+
 struct WsHeader {
+    // line 0
     int32_t invalid_ids;      // ids outside [0, num_embeddings) seen by the last call
     int32_t num_chunks;       // chunks of all runs
     int32_t num_long_runs;    // runs longer than kNRows rows
-    int32_t num_long_chunks;  // chunks of those runs = rows of the partial buffer in use
+    int32_t num_long_chunks;  // chunks of those runs
     int32_t num_runs;         // distinct ids
-    uint32_t cost_total;      // sum of the per-tile costs of all chunks
-    int32_t pad0[10];
-    // 64-byte aligned: set to the call's epoch (nonzero) by the sorting
-    // workgroup once the tables are published, back to 0 by the combine kernel
-    // that ends every call
+    int32_t pad0[27];
+    // line 1: published by the sorting workgroup, then `ready` is set to the
+    // call's epoch (nonzero); the last workgroup to finish sets it back to 0
     uint32_t ready;
-    int32_t wait_timeouts;    // workgroups that gave up waiting (never expected)
-    int32_t pad1[46];
+    int32_t wait_timeouts;    // bounded waits that gave up (never expected)
+    uint32_t pub_long_chunks; // long chunks of this call
+    uint32_t pub_long_runs;   // long runs of this call
+    uint32_t pub_tasks;       // combine tasks of this call
+    int32_t pad1[27];
+    // line 2: next batch of long units / next combine task to hand out
+    uint32_t unit_ticket;
+    int32_t pad2a[15];
+    uint32_t task_ticket;
+    int32_t pad2b[15];
+    // line 3: groups of workgroups that have finished
+    uint32_t exit_top;
+    int32_t pad3[31];
+    // lines 4-7: workgroups of each group that have finished, 64 bytes apart
+    uint32_t exit_group[kExitGroups][16];
 };
-static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
-
-// One run longer than kNRows rows: its chunks' partial sums are rows
-// first_partial .. first_partial + nchunks - 1 of the partial buffer.
-struct alignas(16) LongRunDesc {
-    int32_t row;
-    int32_t first_partial;
-    int32_t nchunks;
-    int32_t unused;
-};
-static_assert(sizeof(LongRunDesc) == 16, "long-run descriptor is 16 bytes");
+static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
+static_assert(offsetof(WsHeader, wait_timeouts) == EWG_WS_WAIT_TIMEOUTS_OFFSET,
+              "documented diagnostic word");
 
 // Optional outputs of the sort step (all null in the accumulate path).
 struct SortTables {
@@ -56,26 +70,33 @@ struct SortTables {
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Byte offsets inside the workspace for num_tokens tokens and `hidden` columns.
+// The header has a fixed place; everything after it depends on the sizes and
+// is written by a call before that call reads it.
 struct WsLayout {
-    size_t keys;             // uint32[kMaxTokens]: sorted keys (published by the sorter)
-    size_t info;             // uint32[kMaxTokens]: chunk table
-    size_t cost;             // uint32[kMaxTokens + 1]: exclusive prefix of chunk costs
-    size_t long_runs;        // LongRunDesc[num_tokens / 11 + 1]
+    size_t units;            // 32-byte record per long chunk (positions, rows, run)
+    size_t runs;             // 16-byte record per long run (row, first chunk, chunks, tasks)
+    size_t done;             // per long run: finished units, one 64-byte line each
     size_t partial;          // float[max_long_chunks][partial_stride]
     size_t total;
     int64_t partial_stride;  // floats per partial row
     int64_t max_long_chunks; // a run of L > 10 rows has ceil(L/10) <= 2L/11 chunks
+    int64_t max_long_runs;   // a long run has at least 11 rows
 };
+
+constexpr int kMaxGrid = 4095;       // workgroups of one launch, at most
+constexpr size_t kUnitRecordBytes = 32;
+constexpr size_t kRunRecordBytes = 16;
+constexpr size_t kDoneStride = 16;   // uint32 words between two runs' counters
 
 inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     WsLayout l;
-    l.keys = sizeof(WsHeader);
-    l.info = l.keys + sizeof(uint32_t) * kMaxTokens;
-    l.cost = l.info + sizeof(uint32_t) * kMaxTokens;
-    l.long_runs = round_up(l.cost + sizeof(uint32_t) * (kMaxTokens + 1), 256);
-    l.partial = round_up(l.long_runs + sizeof(LongRunDesc) * (size_t)(num_tokens / 11 + 1), 256);
-    l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
     l.max_long_chunks = 2 * num_tokens / 11;
+    l.max_long_runs = num_tokens / 11;
+    l.units = sizeof(WsHeader);
+    l.runs = round_up(l.units + kUnitRecordBytes * (size_t)(l.max_long_chunks + 1), 256);
+    l.done = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
+    l.partial = round_up(l.done + 4 * kDoneStride * (size_t)(l.max_long_runs + 1), 256);
+    l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
     l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
                                        (size_t)l.max_long_chunks, 256);
     return l;
@@ -88,20 +109,14 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
                               int pos_bits, int id_bits, void *workspace, const WsLayout &l,
                               const SortTables &tables, hipStream_t stream);
 
-// Fused sort + chunk sums over the grad rows; finishes single-chunk runs and
-// writes the long-run list for the combine. One workgroup per compute unit.
-// grad_bf16 / mg_bf16 select the element types; vec selects 16-byte rows.
+// The whole accumulation in one kernel: sort, chunk sums over the grad rows,
+// single-chunk runs finished, ordered combine of long runs. One workgroup per
+// compute unit. grad_bf16 / mg_bf16 select the element types; vec selects
+// 16-byte rows.
 hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
                              const void *ids, int n, int num_embeddings, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
                              int num_cus, uint32_t epoch, hipStream_t stream);
-
-// Ordered combine of the chunk sums of long runs; finishes them and clears
-// the ready flag for the next call.
-hipError_t launch_long_run_sums(bool grad_bf16, bool mg_bf16, bool vec, void *main_grad,
-                                int64_t mg_stride, int hidden, void *workspace,
-                                const WsLayout &l, int max_long_runs, int num_cus,
-                                hipStream_t stream);
 
 }  // namespace ewg

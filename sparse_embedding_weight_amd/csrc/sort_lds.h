@@ -202,11 +202,13 @@ __device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id
     return cur;
 }
 
-// Optional global outputs of the sort step.
+// Optional outputs of the sort step.
 struct SortOutputs {
-    SortTables tables;            // per-slot tables (all null if not wanted)
-    LongRunDesc *long_runs;       // long-run list for the combine kernel (or null)
-    WsHeader *hdr;                // counts (or null)
+    SortTables tables;            // per-slot tables, global (all null if not wanted)
+    WsHeader *hdr;                // counts, global (or null)
+    uint32_t *lc_run;             // LDS: run number of every long chunk (or null)
+    uint32_t *lr;                 // LDS: per long run {main_grad row, first long chunk,
+                                  //      chunk count, 0} (or null)
 };
 
 // Runs, chunks and long runs from the sorted keys. Blocked arrangement:
@@ -290,14 +292,16 @@ __device__ __forceinline__ SortResult mark_runs(SortSmem &sm, int cur, int n, in
                               (longer ? ((uint32_t)lc_idx << 17) | kInfoLong : 0u);
                 if (out.tables.chunk_first) out.tables.chunk_first[1 + c_idx] = s;
             }
-            if (((flag[j] >> 16) & 1) && out.long_runs) {
-                LongRunDesc lr;
-                lr.row = (int32_t)(k[j] >> pos_bits);
-                lr.first_partial = lc_idx;
-                lr.nchunks = (int32_t)((end[j] - first[j] + kNRows - 1) / kNRows);
-                lr.unused = 0;
-                out.long_runs[lr_idx] = lr;
+            if (((flag[j] >> 16) & 1) && out.lr) {
+                out.lr[4 * lr_idx + 0] = k[j] >> pos_bits;
+                out.lr[4 * lr_idx + 1] = (uint32_t)lc_idx;
+                out.lr[4 * lr_idx + 2] = (end[j] - first[j] + kNRows - 1) / kNRows;
+                out.lr[4 * lr_idx + 3] = 0u;
             }
+            // a long chunk belongs to the long run that starts at its slot, or
+            // else to the last one started before it
+            if ((flag[j] >> 32) & 1 && out.lc_run)
+                out.lc_run[lc_idx] = (uint32_t)(((flag[j] >> 16) & 1) ? lr_idx : lr_idx - 1);
             if (((flag[j] >> 16) & 1) && out.tables.long_runs) out.tables.long_runs[1 + lr_idx] = s;
             if (out.tables.sorted_ids) {
                 out.tables.sorted_ids[s] = (int32_t)(k[j] >> pos_bits);
@@ -329,34 +333,6 @@ __device__ __forceinline__ SortResult mark_runs(SortSmem &sm, int cur, int n, in
     }
     __syncthreads();   // chunk_info complete
     return res;
-}
-
-// Exclusive prefix of the per-tile cost of the chunks info[0..count), into
-// out[0..count] (LDS): a chunk of R rows costs R * row_cost + end_cost. Returns
-// the total. Blocked: thread t owns chunks [8t, 8t + 8).
-__device__ __forceinline__ uint32_t chunk_cost_prefix(SortSmem &sm, const uint32_t *info,
-                                                      int count, uint32_t *out,
-                                                      uint32_t row_cost, uint32_t end_cost) {
-    const int c0 = threadIdx.x * kSortItems;
-    uint32_t cost[kSortItems];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const int c = c0 + j;
-        cost[j] = c < count ? (uint32_t)info_rows(info[c]) * row_cost + end_cost : 0u;
-        sum += cost[j];
-    }
-    uint64_t total;
-    uint32_t run = (uint32_t)block_exclusive_scan(sum, sm.scan, &total);
-#pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const int c = c0 + j;
-        if (c < count) out[c] = run;
-        run += cost[j];
-    }
-    if (threadIdx.x == 0) out[count] = (uint32_t)total;
-    __syncthreads();
-    return (uint32_t)total;
 }
 
 // Nothing to accumulate (some id out of range): zero counts, error count.

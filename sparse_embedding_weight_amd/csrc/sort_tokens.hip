@@ -13,9 +13,9 @@ namespace {
 template <typename IdT>
 __global__ __launch_bounds__(kSortThreads) void sort_tokens_kernel(
     const IdT *__restrict__ ids, int n, int num_embeddings, int pos_bits, int id_bits,
-    WsHeader *__restrict__ hdr, LongRunDesc *__restrict__ long_runs, SortTables tables) {
+    WsHeader *__restrict__ hdr, SortTables tables) {
     __shared__ SortSmem sm;
-    const SortOutputs out = {tables, long_runs, hdr};
+    const SortOutputs out = {tables, hdr, nullptr, nullptr};
     const int bad = load_keys<IdT>(sm, ids, n, num_embeddings, pos_bits);
     if (bad) {
         report_invalid(out, bad);
@@ -32,15 +32,13 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
                               const SortTables &tables, hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws);
-    LongRunDesc *long_runs = reinterpret_cast<LongRunDesc *>(ws + l.long_runs);
+    (void)l;
     if (ids_int64)
         sort_tokens_kernel<int64_t><<<1, kSortThreads, 0, stream>>>(
-            static_cast<const int64_t *>(ids), n, num_embeddings, pos_bits, id_bits, hdr,
-            long_runs, tables);
+            static_cast<const int64_t *>(ids), n, num_embeddings, pos_bits, id_bits, hdr, tables);
     else
         sort_tokens_kernel<int32_t><<<1, kSortThreads, 0, stream>>>(
-            static_cast<const int32_t *>(ids), n, num_embeddings, pos_bits, id_bits, hdr,
-            long_runs, tables);
+            static_cast<const int32_t *>(ids), n, num_embeddings, pos_bits, id_bits, hdr, tables);
     return hipGetLastError();
 }
 

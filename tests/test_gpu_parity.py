@@ -48,14 +48,32 @@ def oracle_rows(ids: torch.Tensor, grad: torch.Tensor, rows: torch.Tensor,
     return mg_np
 
 
+_SHARED_WS = {}
+
+
+def shared_workspace(n: int, hidden: int) -> torch.Tensor:
+    """One workspace reused by every call of this module (grown when needed), so
+    the counters a call leaves behind are exercised by the next call."""
+    need = ewg.workspace_bytes(n, hidden)
+    ws = _SHARED_WS.get("ws")
+    if ws is None or ws.numel() < need:
+        ws = ewg.new_workspace(8192, max(hidden, 7232), "cuda")
+        _SHARED_WS["ws"] = ws
+    return ws
+
+
 def check_call(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor, **kw):
     """Run one call on the GPU and compare with the oracle; returns the touched rows."""
     m_dt = "bf16" if main_grad.dtype == torch.bfloat16 else "fp32"
     rows = torch.unique(ids.reshape(-1).long())
     before_rows = main_grad[rows].clone()
     before = main_grad.clone()
-    ewg.accumulate_embedding_wgrad(ids, grad, main_grad, **kw)
+    ws = kw.pop("workspace", None)
+    if ws is None:
+        ws = shared_workspace(ids.numel(), grad.shape[-1])
+    ewg.accumulate_embedding_wgrad(ids, grad, main_grad, workspace=ws, **kw)
     torch.cuda.synchronize()
+    assert ewg.wait_timeouts(ws) == 0, "a bounded wait inside the kernel gave up"
 
     got = wl.to_numpy_bits(main_grad[rows].cpu())
     want = oracle_rows(ids, grad, rows, before_rows)
@@ -66,8 +84,15 @@ def check_call(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor, *
     mism = (gv != wv) & ~nan_g
     if mism.any():
         r, c = np.argwhere(mism)[0]
-        raise AssertionError(f"{int(mism.sum())} mismatching elements; first at touched row "
-                             f"{r} (id {int(rows[r])}), column {c}: got {gv[r, c]:#x} want {wv[r, c]:#x}")
+        bad_rows = np.flatnonzero(mism.any(axis=1))
+        counts = np.bincount(ids.reshape(-1).long().cpu().numpy())
+        detail = "; ".join(
+            f"id {int(rows[b])} ({int(counts[int(rows[b])])} rows): {int(mism[b].sum())} cols "
+            f"in [{int(np.flatnonzero(mism[b])[0])}, {int(np.flatnonzero(mism[b])[-1])}]"
+            for b in bad_rows[:12])
+        raise AssertionError(f"{int(mism.sum())} mismatching elements in {bad_rows.size} rows; first "
+                             f"at touched row {r} (id {int(rows[r])}), column {c}: got {gv[r, c]:#x} "
+                             f"want {wv[r, c]:#x}; {detail}")
 
     # untouched rows: bit-identical to the copy taken before the call
     changed = (_bits(main_grad) != _bits(before)).any(dim=1)
@@ -215,6 +240,23 @@ def test_repeatable_bitwise():
     ewg.accumulate_embedding_wgrad(ids, grad, b)
     torch.cuda.synchronize()
     assert torch.equal(_bits(a), _bits(b))
+
+
+def test_workspace_reuse_across_shapes():
+    # one workspace through calls of different sizes, types and run structure
+    # (its counters and flag must be left clean by every call)
+    ws = ewg.new_workspace(8192, 2048, "cuda")
+    rng = np.random.default_rng(13)
+    cases = [
+        (8192, 40, 2048, "bf16", "fp32", wl.zipf_ids(rng, 8192, 40, 1.1)),     # all runs long
+        (4097, 5000, 100, "fp32", "bf16", None),                               # mostly short runs
+        (8192, 20000, 1024, "bf16", "bf16", rng.permutation(20000)[:8192]),    # no long run
+        (3073, 3, 7, "fp32", "fp32", None),                                     # 3 long runs, ragged
+        (8192, 129280, 2048, "bf16", "fp32", wl.zipf_ids(rng, 8192, 129280, 1.1)),
+    ]
+    for i, (n, vocab, hidden, gd, md, ids) in enumerate(cases * 2):
+        print(f"[parity] reuse case {i}: n={n} vocab={vocab} hidden={hidden}", flush=True)
+        check_call(*make_case(n, vocab, hidden, gd, md, ids=ids, seed=100 + i), workspace=ws)
 
 
 def test_invalid_ids_change_nothing():
