@@ -125,8 +125,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRawBufferWord3 = 0x00020000;   // untyped 32-bit elements, no swizzle
 constexpr int kDeviceScope = 16;              // cache-policy bits of device scope
 
+// `base` and `bytes` must be the same in every lane of the wave (a buffer
+// resource lives in scalar registers); they are read from the first lane, so
+// the compiler need not guard every access with a loop over distinct values.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes),
                                              kRawBufferWord3);
 }
 
