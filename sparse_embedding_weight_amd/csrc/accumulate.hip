@@ -84,9 +84,16 @@ struct CombineSmem {
     u32x4 runs[kMaxLongRuns + 1];           // run records: row, first chunk, chunks, first task
 };
 
+struct LongSmem {
+    u32x4 rec[2 * kMaxLongChunks];      // unit records of this workgroup's chunks, two halves each
+    uint32_t run_cnt[kMaxLongRuns];     // units of each long run this workgroup has finished
+    uint32_t claim;                     // next unit of this workgroup's share to claim
+};
+
 union AccSmem {
     SortSmem sort;
     FollowerSmem fol;
+    LongSmem lng;
     CombineSmem comb;
 };
 
@@ -556,11 +563,11 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
         }
         uint64_t total;
         const uint32_t first_task = (uint32_t)block_exclusive_scan(tasks, ss.scan, &total);
-        if (tid < (int)n_lr) {
+        if (tid < (int)n_lr)
             store_coherent16(runs_rs, (uint32_t)tid * kRunRecordBytes,
                              u32x4{lr[4 * tid], lr[4 * tid + 1], chunks, first_task});
-            store_coherent(&done[tid * kDoneStride], 0u);
-        }
+        for (int i = tid; i < (int)n_lr * kDoneGroups; i += kSortThreads)
+            store_coherent(&done[(size_t)i * kDoneStride], 0u);
         n_tasks = (uint32_t)total;
 
     }
@@ -568,7 +575,6 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
         store_coherent(&hdr->pub_long_chunks, n_lc);
         store_coherent(&hdr->pub_long_runs, n_lr);
         store_coherent(&hdr->pub_tasks, n_tasks);
-        store_coherent(&hdr->unit_ticket, 0u);
         store_coherent(&hdr->task_ticket, 0u);
     }
     // every store of every wave has completed, then the flag goes up
@@ -592,88 +598,76 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     return true;
 }
 
-// Long units (chunk c, column tile k) = c * tiles + k, handed out in batches
-// of one unit per wave: thread 0 takes batches from the device-wide ticket
-// (one serialised atomic per batch; the next batch is taken while the
-// current one runs), each wave does one unit of the batch, storing the chunk
-// sums of its columns in partial row c with device-coherent stores, and once
-// all have completed the batch's units are counted for their runs (a batch is
-// contiguous, so units of one run are adjacent: one atomic per run of the
-// batch). Workgroups that come late find the tickets gone, which evens out
-// the end of the short-run phase; single-tile units keep the last batches
-// short.
+// Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
+// takes units [w * U / W, (w + 1) * U / W) of the U = chunks * tiles units:
+// the shares are fixed by the published chunk count alone, so no device-wide
+// counter is touched while the units run (a device-scope atomic in a wave
+// also holds back that wave's next loads until it returns). The records of
+// the share's chunks are copied to LDS, then the waves claim units one at a
+// time with an LDS counter. Each unit's fp32 chunk sums go to its partial
+// row with device-coherent stores. The finished units are counted per run
+// in LDS and added to the run's counter of this workgroup's group once,
+// after all stores of the workgroup have completed.
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ void long_units(uint32_t *s_word, uint32_t *s_run,
-                                           WsHeader *__restrict__ hdr,
+__device__ __forceinline__ void long_units(LongSmem &ls, WsHeader *__restrict__ hdr,
                                            __amdgpu_buffer_rsrc_t units_rs,
-                                           uint32_t *__restrict__ done, uint32_t total,
+                                           uint32_t *__restrict__ done, uint32_t n_lc,
                                            uint32_t n_lr, int n,
                                            const typename G::T *__restrict__ grad,
                                            int64_t grad_stride, float *__restrict__ partial,
                                            int64_t partial_stride, int hidden, int tiles,
                                            uint32_t epoch) {
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
     const int full_tiles = hidden / (64 * VEC);
-    constexpr uint32_t kBatch = kSortWaves;
-    // batch numbers alternate between two LDS words: the one written during a
-    // batch is read after its closing barrier, and rewritten only a batch later
-    if (tid == 0) {
-        uint32_t b = load_coherent(&hdr->unit_ticket);   // a plain look first
-        if (b < total) b = fetch_add_coherent(&hdr->unit_ticket, kBatch);
-        s_word[2] = b;
-    }
+    const uint32_t total = n_lc * (uint32_t)tiles;
+    const uint32_t lo = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
+    const uint32_t hi = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
+    const uint32_t c_lo = lo / (uint32_t)tiles;
+    const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;   // chunks [c_lo, c_hi)
+    for (uint32_t i = (uint32_t)tid; i < 2 * (c_hi - c_lo); i += kSortThreads)
+        ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
+    for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) ls.run_cnt[r] = 0u;
+    if (tid == 0) ls.claim = 0u;
     __syncthreads();
-    uint32_t b = s_word[2];
-    for (int k = 1; b < total; ++k) {   // uniform
-        uint32_t next = 0;
-        if (tid == 0) next = fetch_add_coherent(&hdr->unit_ticket, kBatch);
-        const uint32_t t = b + (uint32_t)wave;
-        uint32_t run = 0xffffffffu;
-        if (t < total) {
-            const uint32_t c = t / (uint32_t)tiles;
-            const int tile = (int)(t - c * (uint32_t)tiles);
-            const u32x4 ra = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes);
-            const u32x4 rb = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes + 16);
-            uint32_t w[6] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y};
+
+    // every branch below is on a wave-uniform value; the single-lane LDS
+    // updates are whole-wave atomics in which only lane 0 adds anything
+    const uint32_t one = lane == 0 ? 1u : 0u;
+    for (;;) {
+        const uint32_t u = lo + __builtin_amdgcn_readfirstlane(atomicAdd(&ls.claim, one));
+        if (u >= hi) break;
+        const uint32_t c = u / (uint32_t)tiles;
+        const int tile = (int)(u - c * (uint32_t)tiles);
+        const u32x4 ra = ls.rec[2 * (c - c_lo)], rb = ls.rec[2 * (c - c_lo) + 1];
+        uint32_t w[6] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y};
 #pragma unroll
-            for (int i = 0; i < 6; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
-            int rows = (int)(w[5] & 0xffffu);
-            rows = rows < 1 ? 1 : (rows > kNRows ? kNRows : rows);
-            int32_t pos[kNRows];
+        for (int q = 0; q < 6; ++q) w[q] = __builtin_amdgcn_readfirstlane(w[q]);
+        int rows = (int)(w[5] & 0xffffu);
+        rows = rows < 1 ? 1 : (rows > kNRows ? kNRows : rows);
+        int32_t pos[kNRows];
 #pragma unroll
-            for (int r = 0; r < kNRows; ++r) {
-                const uint32_t q = (w[r >> 1] >> (16 * (r & 1))) & 0xffffu;
-                pos[r] = q < (uint32_t)n ? (int32_t)q : 0;   // every row inside grad
-            }
-            // a record of another call (never expected) is counted and its unit skipped
-            if (__builtin_amdgcn_readfirstlane(rb.w) == epoch) {
-                chunk_tiles_any<G, M, VEC>(pos, rows, 0, (int)c, grad, grad_stride, nullptr, 0,
-                                           partial, partial_stride, hidden, tile, tile + 1,
-                                           full_tiles);
-                run = w[5] >> 16;
-            } else if ((tid & 63) == 0) {
-                fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-            }
+        for (int r = 0; r < kNRows; ++r) {
+            const uint32_t q = (w[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+            pos[r] = q < (uint32_t)n ? (int32_t)q : 0;   // every row inside grad
         }
-        // runs of the batch's units, in the buffer of this batch's parity: a wave
-        // without a unit in the next batch writes at once, while wave 0 may
-        // still be counting this one
-        uint32_t *runs_k = s_run + (k & 1) * kSortWaves;
-        if ((tid & 63) == 0) runs_k[wave] = run;
-        if (tid == 0) s_word[2 + (k & 1)] = next;
-        // the chunk sums of every wave have completed before they are counted
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid < kSortWaves) {
-            const uint32_t r = runs_k[tid];
-            if (r < n_lr && (tid == 0 || runs_k[tid - 1] != r)) {
-                uint32_t m = 1;
-                while (tid + (int)m < kSortWaves && runs_k[tid + m] == r) ++m;
-                fetch_add_coherent(&done[r * kDoneStride], m);
-            }
+        const uint32_t run = w[5] >> 16;
+        // a record of another call (never expected) is counted and its unit skipped
+        if (__builtin_amdgcn_readfirstlane(rb.w) == epoch && run < n_lr) {
+            chunk_tiles_any<G, M, VEC>(pos, rows, 0, (int)c, grad, grad_stride, nullptr, 0,
+                                       partial, partial_stride, hidden, tile, tile + 1,
+                                       full_tiles);
+            atomicAdd(&ls.run_cnt[run], one);
+        } else {
+            fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), one);
         }
-        b = s_word[2 + (k & 1)];
+    }
+    // the chunk sums of every wave have completed before they are counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const size_t grp = blockIdx.x % kDoneGroups;
+    for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) {
+        const uint32_t m = ls.run_cnt[r];
+        if (m) fetch_add_coherent(&done[((size_t)r * kDoneGroups + grp) * kDoneStride], m);
     }
 }
 
@@ -732,7 +726,11 @@ __device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
             int ok = valid ? 1 : 0;
             const uint32_t target = chunks * (uint32_t)tiles;
             int64_t spins = 0;
-            while (ok && load_coherent(&done[lo * kDoneStride]) < target) {
+            for (;;) {
+                uint32_t sum = 0;
+                for (int g = 0; g < kDoneGroups; ++g)
+                    sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
+                if (!ok || sum >= target) break;
                 __builtin_amdgcn_s_sleep(2);
                 if (++spins > kWaitLimit) {
                     fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
@@ -797,7 +795,17 @@ __device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
                         const int j = tid + i * kSortThreads;
                         const float *col = &cs.stage[j < wc ? j : wave_j0];
                         float acc = total[i];
-                        for (int kk = 0; kk < ks; ++kk) acc = acc + col[kk * wdt];
+                        // the adds stay in chunk order; the LDS reads of a group
+                        // of 8 are all issued before the first add
+                        int kk = 0;
+                        for (; kk + 8 <= ks; kk += 8) {
+                            float v[8];
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) v[q] = col[(kk + q) * wdt];
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) acc = acc + v[q];
+                        }
+                        for (; kk < ks; ++kk) acc = acc + col[kk * wdt];
                         total[i] = acc;
                     }
                 }
@@ -823,7 +831,6 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     int64_t partial_stride, uint32_t epoch) {
     __shared__ AccSmem sm;
     __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
-    __shared__ uint32_t s_run[2 * kSortWaves];
     const int tid = threadIdx.x;
     const uint32_t n_lc_max = (uint32_t)(2 * n / 11), n_lr_max = (uint32_t)(n / 11);
     const __amdgpu_buffer_rsrc_t units_rs = buffer_range(units, n_lc_max * (uint32_t)kUnitRecordBytes);
@@ -846,8 +853,8 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     if (s_word[0] == 0u) {   // uniform: every wave saw the flag
         const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
         const uint32_t n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
-        long_units<G, M, VEC>(s_word, s_run, hdr, units_rs, done, n_lc * (uint32_t)tiles, n_lr, n,
-                              grad, grad_stride, partial, partial_stride, hidden, tiles, epoch);
+        long_units<G, M, VEC>(sm.lng, hdr, units_rs, done, n_lc, n_lr, n, grad, grad_stride,
+                              partial, partial_stride, hidden, tiles, epoch);
     }
     __syncthreads();
     combine_tasks<G, M>(sm.comb, s_word, hdr, runs_rs, done, partial, partial_stride, main_grad,
@@ -868,7 +875,6 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
         if (last) {
             for (int g = 0; g < kExitGroups; ++g) store_coherent(&hdr->exit_group[g][0], 0u);
             store_coherent(&hdr->exit_top, 0u);
-            store_coherent(&hdr->unit_ticket, 0u);
             store_coherent(&hdr->task_ticket, 0u);
             store_coherent(&hdr->ready, 0u);
         }

@@ -42,11 +42,9 @@ struct WsHeader {
     uint32_t pub_long_runs;   // long runs of this call
     uint32_t pub_tasks;       // combine tasks of this call
     int32_t pad1[27];
-    // line 2: next batch of long units / next combine task to hand out
-    uint32_t unit_ticket;
-    int32_t pad2a[15];
+    // line 2: next combine task to hand out
     uint32_t task_ticket;
-    int32_t pad2b[15];
+    int32_t pad2[31];
     // line 3: groups of workgroups that have finished
     uint32_t exit_top;
     int32_t pad3[31];
@@ -75,7 +73,7 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
     size_t units;            // 32-byte record per long chunk (positions, rows, run)
     size_t runs;             // 16-byte record per long run (row, first chunk, chunks, tasks)
-    size_t done;             // per long run: finished units, one 64-byte line each
+    size_t done;             // per long run: finished units, kDoneGroups counters of 128 bytes
     size_t partial;          // float[max_long_chunks][partial_stride]
     size_t total;
     int64_t partial_stride;  // floats per partial row
@@ -86,7 +84,8 @@ struct WsLayout {
 constexpr int kMaxGrid = 4095;       // workgroups of one launch, at most
 constexpr size_t kUnitRecordBytes = 32;
 constexpr size_t kRunRecordBytes = 16;
-constexpr size_t kDoneStride = 16;   // uint32 words between two runs' counters
+constexpr size_t kDoneStride = 32;   // uint32 words between two unit counters (128 bytes)
+constexpr int kDoneGroups = 8;       // unit counters per long run: one per group of workgroups
 
 inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     WsLayout l;
@@ -95,7 +94,7 @@ inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     l.units = sizeof(WsHeader);
     l.runs = round_up(l.units + kUnitRecordBytes * (size_t)(l.max_long_chunks + 1), 256);
     l.done = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
-    l.partial = round_up(l.done + 4 * kDoneStride * (size_t)(l.max_long_runs + 1), 256);
+    l.partial = round_up(l.done + 4 * kDoneStride * kDoneGroups * (size_t)(l.max_long_runs + 1), 256);
     l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
     l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
                                        (size_t)l.max_long_chunks, 256);
