@@ -136,8 +136,11 @@ size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hi
  * other workgroups finish every run of at most EWG_NROWS rows; then all of
  * them sum the chunks of the long runs and add those sums in chunk order.
  * Workgroups hand work to each other through the workspace, and every wait in
- * the kernel is bounded. Any alignment is accepted; 16-byte aligned rows take
- * the vector path.
+ * the kernel is bounded; the waits end in time when the launch's workgroups
+ * run together (one per compute unit: the stream must not be restricted to
+ * fewer compute units). A wait that gives up is counted in the workspace's
+ * int32 at EWG_WS_WAIT_TIMEOUTS_OFFSET and its work is skipped. Any alignment
+ * is accepted; 16-byte aligned rows take the vector path.
  *
  * The workspace carries counters from one call to the next: a call that did
  * not run to completion (for example a device fault) leaves it unusable

@@ -21,28 +21,29 @@
 //      and finishes its equal-cost share of the runs of at most 10 rows (a run
 //      of at most 10 rows is one chunk: it needs its rows in position order,
 //      not a global sort).
-//   3. Each wave that is done waits for the flag; then the workgroup takes
-//      batches of (long chunk, column group) units, one per wave, from a
-//      ticket counter, stores their fp32 chunk sums in the partial buffer with
-//      device-coherent stores and adds to each run's counter how many of its
-//      units the batch finished. Workgroups whose short runs took longer find
-//      fewer batches left.
+//   3. Each wave that is done waits for the flag; then every workgroup takes
+//      a fixed share of the (long chunk, column tile) units, stores their fp32
+//      chunk sums in the partial buffer with device-coherent stores and, once
+//      they have completed, adds its count of each run's units to that run's
+//      counter for its group of workgroups.
 //   4. Then whole workgroups take combine tasks (one long run, one block of
 //      columns) from a ticket counter: wait until the run's units are all
 //      counted, stage its chunk sums in LDS, add them in chunk order from +0,
 //      round, add to main_grad, round.
-//   5. The last workgroup to finish clears the tickets, the exit counters and
+//   5. The last workgroup to finish clears the ticket, the exit counters and
 //      the flag for the next call. (These live in the workspace header, whose
 //      place does not depend on the sizes of a call; the per-run counters do,
 //      so workgroup 0 zeroes them before it raises the flag.)
-// Device-scope atomics on one address are serialised, so the kernel uses
-// LDS atomics for the fine-grained claims and touches every shared counter
-// about once per workgroup or batch. No wait can deadlock: the flag is raised
-// by workgroup 0, which waits for nothing before it; a combine task waits
-// only for units of batches that running workgroups have already taken, and
-// a taken batch never waits. So the launch needs no particular number of
-// resident workgroups. Every wait is bounded; a wait that gives up is counted
-// in the workspace header and its work skipped.
+// Device-scope atomics on one address are serialised, and a wave's atomic
+// that returns a value also holds back its later loads (the vector memory
+// counter drains in order), so the kernel claims fine-grained work through
+// LDS counters and touches every shared counter about once per workgroup.
+// The flag is raised by workgroup 0, which waits for nothing before it; a
+// combine task waits only for the long units of the shares of other
+// workgroups, which wait for nothing but the flag, so every wait ends as long
+// as the launch's workgroups are resident together (one per compute unit, as
+// launched). Every wait is bounded; a wait that gives up is counted in the
+// workspace header and its work skipped.
 //
 // A column tile is 64 lanes x VEC columns (8 for bf16 grad, 4 for fp32), laid
 // out in lane-contiguous pieces (piece_cols in ewg_device.h).
