@@ -47,6 +47,8 @@ def parse_args():
     p.add_argument("--flush", choices=["read", "write", "none"], default="read",
                    help="how the caches are emptied before each step: read (default) or write a "
                         "1 GiB buffer, or not at all")
+    p.add_argument("--no-dense-baseline", action="store_true",
+                   help="skip timing PyTorch's dense embedding backward + main_grad.add_")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference for counter scaling)")
     return p.parse_args()
@@ -123,6 +125,32 @@ def cpu_baseline(w, ids_np, grad_np, budget_s):
         oracle.accumulate_embedding_wgrad(compact, grad_np, m, w.grad_dtype, w.main_grad_dtype)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), len(times)
+
+
+def dense_baseline(torch, w, ids, grad, mg, flush, flush_sink, flush_mode, our_ms, calls=5):
+    """The path the fused call replaces, on the same GPU and inputs: PyTorch-ROCm's
+    aten::embedding_dense_backward (a zero-filled [vocab, hidden] gradient in grad's
+    dtype) followed by main_grad.add_ over the whole table. Timed with events on the
+    current stream, caches emptied before each call as for the fused call."""
+    times = []
+    for k in range(calls + 1):
+        if flush_mode == "read":
+            flush_sink.copy_(flush.sum())
+        elif flush_mode == "write":
+            flush.fill_(float(k))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gw = torch.ops.aten.embedding_dense_backward(grad, ids.long(), w.vocab, -1, False)
+        mg.add_(gw)
+        e1.record()
+        torch.cuda.synchronize()
+        del gw
+        if k:   # the first call warms up
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.mean(times))
+    return {"us_per_call": round(ms * 1e3, 1), "calls": calls,
+            "kind": "aten::embedding_dense_backward + main_grad.add_ (PyTorch-ROCm)",
+            "speedup_of_fused_call": round(ms / our_ms, 2)}
 
 
 def main():
@@ -225,6 +253,10 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "traffic": measured_traffic(name)},
     }
+
+    if not args.no_dense_baseline:
+        result["dense_baseline"] = dense_baseline(torch, w, ids, grad, mg, flush, flush_sink,
+                                                  args.flush, mean_call_ms)
 
     if not args.no_cpu_baseline:
         t_cpu, reps = cpu_baseline(w, ids_np, wl.to_numpy_bits(grad_cpu), args.cpu_seconds)
