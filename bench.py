@@ -47,6 +47,9 @@ def parse_args():
     p.add_argument("--flush", choices=["read", "write", "none"], default="read",
                    help="how the caches are emptied before each step: read (default) or write a "
                         "1 GiB buffer, or not at all")
+    p.add_argument("--vocab-shards", type=int, default=0,
+                   help="also time the vocabulary-shard entry point: the table split into this "
+                        "many equal row ranges, one call per shard (reported under vocab_shards)")
     p.add_argument("--no-dense-baseline", action="store_true",
                    help="skip timing PyTorch's dense embedding backward + main_grad.add_")
     p.add_argument("--copy-calibration", action="store_true",
@@ -125,6 +128,43 @@ def cpu_baseline(w, ids_np, grad_np, budget_s):
         oracle.accumulate_embedding_wgrad(compact, grad_np, m, w.grad_dtype, w.main_grad_dtype)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)), len(times)
+
+
+def time_vocab_shards(torch, ewg, wl, w, ids, ids_np, grad, mg, flush, flush_sink, flush_mode,
+                      shards, steps, warmup):
+    """Each of `shards` equal row ranges of the table through the vocabulary-shard entry
+    point, as one device of a row-sharded table would call it (the whole batch of ids,
+    its own rows). Per shard: mean µs per call (events on the current stream, caches
+    emptied before each call) and GB/s of that shard's algorithmic bytes."""
+    bounds = [w.vocab * k // shards for k in range(shards + 1)]
+    ws = ewg.new_workspace(w.num_tokens, w.hidden, mg.device)
+    out = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        in_shard = (ids_np >= lo) & (ids_np < hi)
+        uniq = int(np.unique(ids_np[in_shard]).size)
+        alg = wl.algorithmic_bytes(int(in_shard.sum()), w.hidden, uniq, w.grad_dtype,
+                                   w.main_grad_dtype, 0) + ids_np.size * ids_np.itemsize
+        view = mg[lo:hi]
+        times = []
+        for k in range(warmup + steps):
+            if flush_mode == "read":
+                flush_sink.copy_(flush.sum())
+            elif flush_mode == "write":
+                flush.fill_(float(k))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ewg.accumulate_embedding_wgrad_vocab_shard(ids, grad, view, lo, workspace=ws)
+            e1.record()
+            if k >= warmup:
+                times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in times]))
+        out.append({"rows": [lo, hi], "tokens_in_shard": int(in_shard.sum()), "distinct_ids": uniq,
+                    "algorithmic_bytes": alg, "us_per_call": round(ms * 1e3, 2),
+                    "GB_per_s": round(alg / (ms * 1e-3) / 1e9, 1)})
+    if ewg.wait_timeouts(ws):
+        raise RuntimeError("bounded waits gave up inside the kernel (vocabulary shards)")
+    return {"shards": shards, "per_shard": out}
 
 
 def dense_baseline(torch, w, ids, grad, mg, flush, flush_sink, flush_mode, our_ms, calls=5):
@@ -253,6 +293,11 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "traffic": measured_traffic(name)},
     }
+
+    if args.vocab_shards > 1:
+        result["vocab_shards"] = time_vocab_shards(torch, ewg, wl, w, ids, ids_np, grad, mg, flush,
+                                                   flush_sink, args.flush, args.vocab_shards,
+                                                   args.steps, args.warmup)
 
     if not args.no_dense_baseline:
         result["dense_baseline"] = dense_baseline(torch, w, ids, grad, mg, flush, flush_sink,

@@ -166,6 +166,36 @@ int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *ma
                                      hipStream_t stream, hipEvent_t *events);
 
 /*
+ * Vocabulary-sharded form (the embedding table split by rows over devices):
+ * main_grad holds only the shard_rows rows of ids [vocab_start, vocab_start +
+ * shard_rows) of the full table, row v for id vocab_start + v. ids and grad
+ * are the whole batch (num_tokens positions, as in accumulate_embedding_wgrad).
+ * Ids outside the shard are left out: their grad rows are not read and no
+ * row is touched for them; an id in the shard is accumulated with exactly the
+ * arithmetic of accumulate_embedding_wgrad (its run, chunks and their order
+ * depend only on its own positions), so the shards of any partition of the
+ * vocabulary together give, bit for bit, the rows of one unsharded call.
+ *
+ * can_accumulate_embedding_wgrad_vocab_shard: as can_accumulate_embedding_wgrad
+ * with num_embeddings replaced by shard_rows, plus vocab_start >= 0; the
+ * packing test takes one more id bit: (shard_rows << position_bits) |
+ * (num_tokens - 1) < 2^31. No id is invalid here, so the workspace's
+ * invalid-id count stays 0. Workspace, stream, errors: as for
+ * accumulate_embedding_wgrad.
+ */
+int can_accumulate_embedding_wgrad_vocab_shard(int64_t num_tokens, int64_t hidden,
+                                               int64_t vocab_start, int64_t shard_rows,
+                                               int ids_dtype, int grad_dtype, int main_grad_dtype);
+
+int accumulate_embedding_wgrad_vocab_shard(const void *ids, const void *grad, void *main_grad,
+                                           int64_t num_tokens, int64_t hidden,
+                                           int64_t vocab_start, int64_t shard_rows,
+                                           int64_t grad_row_stride, int64_t main_grad_row_stride,
+                                           int ids_dtype, int grad_dtype, int main_grad_dtype,
+                                           void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
+/*
  * Only the sort step, with its tables written out for inspection (page,
  * _sort_tokens_kernel: sort the (token, position) pairs, give every sorted
  * slot the first and last slot of its token's run, list the runs longer than

@@ -13,7 +13,9 @@ from ._binding import (  # noqa: F401
     NROWS,
     EmbeddingWgradError,
     accumulate_embedding_wgrad,
+    accumulate_embedding_wgrad_vocab_shard,
     can_accumulate_embedding_wgrad,
+    can_accumulate_embedding_wgrad_vocab_shard,
     invalid_id_count,
     new_workspace,
     position_bits,

@@ -37,6 +37,8 @@ EXPORTS = (
     "accumulate_embedding_wgrad_workspace_bytes",
     "accumulate_embedding_wgrad",
     "accumulate_embedding_wgrad_timed",
+    "can_accumulate_embedding_wgrad_vocab_shard",
+    "accumulate_embedding_wgrad_vocab_shard",
     "accumulate_embedding_wgrad_sort_tokens",
     "ewg_status_string",
 )
@@ -54,6 +56,11 @@ lib.accumulate_embedding_wgrad.argtypes = _ACC_ARGS
 lib.accumulate_embedding_wgrad.restype = _int
 lib.accumulate_embedding_wgrad_timed.argtypes = _ACC_ARGS + [_vp]
 lib.accumulate_embedding_wgrad_timed.restype = _int
+lib.can_accumulate_embedding_wgrad_vocab_shard.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int]
+lib.can_accumulate_embedding_wgrad_vocab_shard.restype = _int
+lib.accumulate_embedding_wgrad_vocab_shard.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                                       _i64, _int, _int, _int, _vp, _sz, _vp]
+lib.accumulate_embedding_wgrad_vocab_shard.restype = _int
 lib.accumulate_embedding_wgrad_sort_tokens.argtypes = [_vp, _i64, _i64, _int] + [_vp] * 6 + [_vp, _sz, _vp]
 lib.accumulate_embedding_wgrad_sort_tokens.restype = _int
 lib.ewg_status_string.argtypes = [_int]
@@ -169,6 +176,58 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
             _stream_handle(main_grad.device))
     if st != EWG_OK:
         raise EmbeddingWgradError(st, "accumulate_embedding_wgrad")
+
+
+def _same_layout(ids, grad, main_grad) -> bool:
+    if not (isinstance(ids, torch.Tensor) and isinstance(grad, torch.Tensor)
+            and isinstance(main_grad, torch.Tensor)):
+        return False
+    if not _same_gpu(ids, grad, main_grad):
+        return False
+    if ids.dtype not in (torch.int32, torch.int64):
+        return False
+    if grad.dtype not in (torch.bfloat16, torch.float32) or main_grad.dtype not in (torch.bfloat16, torch.float32):
+        return False
+    if grad.dim() != ids.dim() + 1 or tuple(grad.shape[:-1]) != tuple(ids.shape):
+        return False
+    return main_grad.dim() == 2 and main_grad.shape[1] == grad.shape[-1] and main_grad.stride(1) == 1
+
+
+def can_accumulate_embedding_wgrad_vocab_shard(ids: torch.Tensor, grad: torch.Tensor,
+                                               main_grad_shard: torch.Tensor,
+                                               vocab_start: int) -> bool:
+    """Whether accumulate_embedding_wgrad_vocab_shard supports these tensors: as
+    can_accumulate_embedding_wgrad with main_grad_shard's rows standing for ids
+    [vocab_start, vocab_start + rows), vocab_start >= 0, and one more id bit in the
+    31-bit packing test."""
+    if not _same_layout(ids, grad, main_grad_shard) or int(vocab_start) < 0:
+        return False
+    return bool(lib.can_accumulate_embedding_wgrad_vocab_shard(
+        ids.numel(), grad.shape[-1], int(vocab_start), main_grad_shard.shape[0],
+        DTYPE_CODE[ids.dtype], DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad_shard.dtype]))
+
+
+def accumulate_embedding_wgrad_vocab_shard(ids: torch.Tensor, grad: torch.Tensor,
+                                           main_grad_shard: torch.Tensor, vocab_start: int,
+                                           workspace: torch.Tensor = None) -> None:
+    """The rows of one vocabulary shard: main_grad_shard[v] (id vocab_start + v) +=
+    the embedding weight gradient of that id; ids outside the shard are left out.
+    Same arithmetic, bit for bit, as accumulate_embedding_wgrad on the full table.
+    Other arguments and behaviour as for accumulate_embedding_wgrad."""
+    if not can_accumulate_embedding_wgrad_vocab_shard(ids, grad, main_grad_shard, vocab_start):
+        raise ValueError("accumulate_embedding_wgrad_vocab_shard: unsupported inputs "
+                         "(see can_accumulate_embedding_wgrad_vocab_shard)")
+    n, hidden = ids.numel(), grad.shape[-1]
+    ids_flat, grad2 = _flat_inputs(ids, grad)
+    ws = _workspace(n, hidden, main_grad_shard.device, workspace)
+    with torch.cuda.device(main_grad_shard.device):
+        st = lib.accumulate_embedding_wgrad_vocab_shard(
+            ids_flat.data_ptr(), grad2.data_ptr(), main_grad_shard.data_ptr(), n, hidden,
+            int(vocab_start), main_grad_shard.shape[0], grad2.stride(0), main_grad_shard.stride(0),
+            DTYPE_CODE[ids.dtype], DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad_shard.dtype],
+            ws.data_ptr(), ws.numel(), _stream_handle(main_grad_shard.device))
+    if st != EWG_OK:
+        raise EmbeddingWgradError(st, "accumulate_embedding_wgrad_vocab_shard")
 
 
 def sort_tokens(ids: torch.Tensor, num_embeddings: int, workspace: torch.Tensor = None) -> dict:

@@ -60,6 +60,7 @@ constexpr int kHashSlots = 16384;        // > 2 x kMaxTokens: linear probing alw
 constexpr int kHashBits = 14;
 constexpr int kOwnedMax = 256;           // short runs gathered per round by one follower
 constexpr uint32_t kIdMask = (1u << 20) - 1;   // key word: id + 1 in 20 bits, round mark above
+constexpr uint32_t kNoSlot = 0xffffu;    // slot of a position whose id is left out
 constexpr int kStageFloats = 32768;      // combine staging: 128 KiB of chunk sums
 constexpr int kMaxCombineCols = 8192;    // columns of one combine task (8 per thread)
 constexpr int kMaxLongRuns = kMaxTokens / 11;
@@ -284,7 +285,8 @@ __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, i
 // put in order, and the runs finished in main_grad.
 template <typename IdT, typename G, typename M, int VEC>
 __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT *__restrict__ ids,
-                                                    int n, int num_embeddings,
+                                                    int n, int num_embeddings, int64_t id_base,
+                                                    bool skip_outside,
                                                     const typename G::T *__restrict__ grad,
                                                     int64_t grad_stride,
                                                     typename M::T *__restrict__ main_grad,
@@ -308,20 +310,23 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
     if (tid == 0) fs.bad = 0;
     __syncthreads();
 
-    // insert: occurrences per id, slot per position
+    // insert: occurrences per id, slot per position (kNoSlot for a position
+    // whose id is left out)
     int bad = 0;
     uint32_t slot[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int p = i * kSortThreads + tid;
-        slot[i] = 0;
+        slot[i] = kNoSlot;
         if (p >= n) continue;
-        if (id[i] < 0 || id[i] >= num_embeddings) {
-            ++bad;
+        const int64_t v = id[i] - id_base;
+        if (v < 0 || v >= num_embeddings) {
+            if (!skip_outside) ++bad;
+            fs.slot_of_pos[p] = (uint16_t)kNoSlot;
             continue;
         }
-        const uint32_t k1 = (uint32_t)id[i] + 1u;
-        uint32_t h = hash_home((uint32_t)id[i]);
+        const uint32_t k1 = (uint32_t)v + 1u;
+        uint32_t h = hash_home((uint32_t)v);
         for (;;) {
             const uint32_t cur = fs.key[h];
             if (cur == k1) break;
@@ -353,7 +358,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int p = i * kSortThreads + tid;
-        if (p < n) {
+        if (p < n && slot[i] != kNoSlot) {
             const uint32_t w = fs.cnt[slot[i]];
             if ((w & 0xffffu) <= (uint32_t)kNRows && (w >> 16) > (uint32_t)p)
                 atomicMin(&fs.cnt[slot[i]], ((uint32_t)p << 16) | (w & 0xffffu));
@@ -382,8 +387,9 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         for (int j = 0; j < kSortItems; ++j) {
             const int p = p0 + j;
             v[j] = 0;
-            if (p < n) {
-                const uint32_t w = fs.cnt[fs.slot_of_pos[p]];
+            const uint32_t h = p < n ? fs.slot_of_pos[p] : kNoSlot;
+            if (h != kNoSlot) {
+                const uint32_t w = fs.cnt[h];
                 const uint32_t c = w & 0xffffu;
                 if ((w >> 16) == (uint32_t)p && c <= (uint32_t)kNRows)
                     v[j] = (uint64_t)(c * row_cost + end_cost) | (1ull << 32);
@@ -441,7 +447,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 #pragma unroll
         for (int i = 0; i < kSortItems; ++i) {
             const int p = i * kSortThreads + tid;
-            if (p >= n) continue;
+            if (p >= n || fs.slot_of_pos[p] == kNoSlot) continue;
             const uint32_t m = fs.key[fs.slot_of_pos[p]] >> 20;
             if (m) {
                 const uint32_t k = atomicAdd(&fs.run_len[m - 1u], 1u);
@@ -503,7 +509,8 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 // range there is nothing to do: all counts are 0.
 template <typename IdT>
 __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restrict__ ids, int n,
-                                               int num_embeddings, int pos_bits, int id_bits,
+                                               int num_embeddings, int64_t id_base,
+                                               bool skip_outside, int pos_bits, int id_bits,
                                                int hidden, WsHeader *__restrict__ hdr,
                                                __amdgpu_buffer_rsrc_t units_rs,
                                                __amdgpu_buffer_rsrc_t runs_rs,
@@ -512,7 +519,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
     uint32_t n_lc = 0, n_lr = 0, n_tasks = 0;
     const SortOutputs out0 = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
                               nullptr, nullptr};
-    const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits);
+    const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits, id_base, skip_outside);
     if (bad) {
         report_invalid(out0, bad);
     } else {
@@ -527,7 +534,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
                       "long-run tables fit the sort's counter space");
         const SortOutputs out = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
                                  lc_run, lr};
-        const SortResult res = mark_runs(ss, cur, n, pos_bits, out);
+        const SortResult res = mark_runs(ss, cur, ss.n_keys, pos_bits, out);
         for (int c = tid; c < res.n_chunks; c += kSortThreads) {
             const uint32_t x = res.chunk_info[c];
             if (x & kInfoLong) lc_info[info_long_chunk(x)] = x;
@@ -824,7 +831,8 @@ __device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
 
 template <typename IdT, typename G, typename M, int VEC>
 __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
-    const IdT *__restrict__ ids, int n, int num_embeddings, int pos_bits, int id_bits,
+    const IdT *__restrict__ ids, int n, int num_embeddings, int64_t id_base, int skip_outside,
+    int pos_bits, int id_bits,
     const typename G::T *__restrict__ grad, int64_t grad_stride,
     typename M::T *__restrict__ main_grad, int64_t mg_stride, int hidden, int tiles,
     WsHeader *__restrict__ hdr, uint8_t *__restrict__ units,
@@ -840,10 +848,12 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
 
     bool ready = true;
     if (blockIdx.x == 0) {
-        leader_publish<IdT>(sm.sort, ids, n, num_embeddings, pos_bits, id_bits, hidden, hdr,
+        leader_publish<IdT>(sm.sort, ids, n, num_embeddings, id_base, skip_outside != 0, pos_bits,
+                            id_bits, hidden, hdr,
                             units_rs, runs_rs, done, epoch);
     } else {
-        follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, grad, grad_stride,
+        follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
+                                            skip_outside != 0, grad, grad_stride,
                                             main_grad, mg_stride, hidden, tiles,
                                             (int)blockIdx.x - 1, (int)gridDim.x - 1);
         ready = wave_wait_ready(hdr, epoch);
@@ -883,7 +893,8 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
 }
 
 template <typename IdT, typename G, typename M, int VEC>
-hipError_t launch(const void *ids, int n, int num_embeddings, int pos_bits, int id_bits,
+hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, int skip_outside,
+                  int pos_bits, int id_bits,
                   const void *grad, int64_t grad_stride, void *main_grad, int64_t mg_stride,
                   int hidden, void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
                   hipStream_t stream) {
@@ -891,7 +902,7 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int pos_bits, int 
     const int tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
     const int grid = num_cus < 2 ? 2 : (num_cus > kMaxGrid ? kMaxGrid : num_cus);
     accumulate_kernel<IdT, G, M, VEC><<<grid, kSortThreads, 0, stream>>>(
-        static_cast<const IdT *>(ids), n, num_embeddings, pos_bits, id_bits,
+        static_cast<const IdT *>(ids), n, num_embeddings, id_base, skip_outside, pos_bits, id_bits,
         static_cast<const typename G::T *>(grad), grad_stride,
         static_cast<typename M::T *>(main_grad), mg_stride, hidden, tiles,
         reinterpret_cast<WsHeader *>(ws), reinterpret_cast<uint8_t *>(ws + l.units), reinterpret_cast<uint8_t *>(ws + l.runs),
@@ -902,12 +913,14 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int pos_bits, int 
 
 template <typename IdT>
 hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *ids, int n,
-                          int num_embeddings, int pos_bits, int id_bits, const void *grad,
+                          int num_embeddings, int64_t id_base, int skip_outside, int pos_bits,
+                          int id_bits, const void *grad,
                           int64_t grad_stride, void *main_grad, int64_t mg_stride, int hidden,
                           void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
                           hipStream_t stream) {
 #define EWG_ACC(G, M, V)                                                                        \
-    launch<IdT, G, M, V>(ids, n, num_embeddings, pos_bits, id_bits, grad, grad_stride, main_grad, \
+    launch<IdT, G, M, V>(ids, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits, grad,   \
+                         grad_stride, main_grad,                                                  \
                          mg_stride, hidden, workspace, l, num_cus, epoch, stream)
     if (grad_bf16) {
         if (mg_bf16) return vec ? EWG_ACC(BF16, BF16, 8) : EWG_ACC(BF16, BF16, 1);
@@ -921,16 +934,17 @@ hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *id
 }  // namespace
 
 hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
-                             const void *ids, int n, int num_embeddings, int pos_bits, int id_bits,
+                             const void *ids, int n, int num_embeddings, int64_t id_base,
+                             bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
                              int num_cus, uint32_t epoch, hipStream_t stream) {
     if (ids_int64)
-        return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, pos_bits,
-                                       id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
+        return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
+                                       skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
                                        workspace, l, num_cus, epoch, stream);
-    return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, pos_bits,
-                                   id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
+    return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
+                                   skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
                                    workspace, l, num_cus, epoch, stream);
 }
 

@@ -79,11 +79,25 @@ uint32_t next_epoch() {
     return e;
 }
 
+// One call. Unsharded: rows [0, num_embeddings), other ids invalid. Vocabulary
+// shard (shard = true): rows are ids [id_base, id_base + num_embeddings), other
+// ids left out, and the key's id field gets one more bit (so that a kept key
+// never has all id bits set; left-out keys have).
 int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_tokens,
-               int64_t hidden, int64_t num_embeddings, int64_t grad_row_stride,
-               int64_t main_grad_row_stride, int ids_dtype, int grad_dtype, int main_grad_dtype,
-               void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
-    int st = check_common(num_tokens, hidden, num_embeddings, ids_dtype, grad_dtype, main_grad_dtype);
+               int64_t hidden, int64_t num_embeddings, int64_t id_base, bool shard,
+               int64_t grad_row_stride, int64_t main_grad_row_stride, int ids_dtype,
+               int grad_dtype, int main_grad_dtype, void *workspace, size_t workspace_bytes,
+               hipStream_t stream, hipEvent_t *events) {
+    int st = shard ? (!is_known_dtype(ids_dtype) || !is_known_dtype(grad_dtype) ||
+                              !is_known_dtype(main_grad_dtype)
+                          ? EWG_INVALID_ARGUMENT
+                          : (can_accumulate_embedding_wgrad_vocab_shard(num_tokens, hidden, id_base,
+                                                                        num_embeddings, ids_dtype,
+                                                                        grad_dtype, main_grad_dtype)
+                                 ? EWG_OK
+                                 : EWG_UNSUPPORTED))
+                   : check_common(num_tokens, hidden, num_embeddings, ids_dtype, grad_dtype,
+                                  main_grad_dtype);
     if (st != EWG_OK) return st;
     if (!ids || !grad || !main_grad) return EWG_INVALID_ARGUMENT;
     if (grad_row_stride < hidden || main_grad_row_stride < hidden) return EWG_INVALID_ARGUMENT;
@@ -101,12 +115,13 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
     const WsLayout l = ws_layout(num_tokens, hidden);
     const int n = (int)num_tokens;
     const int pos_bits = ewg_position_bits(num_tokens);
-    const int id_bits = bit_length((uint64_t)(num_embeddings - 1));
+    const int id_bits = bit_length((uint64_t)(shard ? num_embeddings : num_embeddings - 1));
 
     (void)hipGetLastError();   // start from a clean per-thread error state
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return EWG_HIP_ERROR;
     st = to_status(launch_accumulate(ids_dtype == EWG_INT64, g_bf16, m_bf16, vec, ids, n,
-                                     (int)num_embeddings, pos_bits, id_bits, grad, grad_row_stride,
+                                     (int)num_embeddings, id_base, shard, pos_bits, id_bits, grad,
+                                     grad_row_stride,
                                      main_grad, main_grad_row_stride, (int)hidden, workspace, l,
                                      num_cus(), next_epoch(), stream));
     if (st != EWG_OK) return st;
@@ -144,9 +159,9 @@ int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_gra
                                int64_t grad_row_stride, int64_t main_grad_row_stride,
                                int ids_dtype, int grad_dtype, int main_grad_dtype,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, grad_row_stride,
-                      main_grad_row_stride, ids_dtype, grad_dtype, main_grad_dtype, workspace,
-                      workspace_bytes, stream, nullptr);
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
+                      grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                      main_grad_dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *main_grad,
@@ -156,9 +171,34 @@ int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *ma
                                      void *workspace, size_t workspace_bytes,
                                      hipStream_t stream, hipEvent_t *events) {
     if (!events) return EWG_INVALID_ARGUMENT;
-    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, grad_row_stride,
-                      main_grad_row_stride, ids_dtype, grad_dtype, main_grad_dtype, workspace,
-                      workspace_bytes, stream, events);
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
+                      grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                      main_grad_dtype, workspace, workspace_bytes, stream, events);
+}
+
+int can_accumulate_embedding_wgrad_vocab_shard(int64_t num_tokens, int64_t hidden,
+                                               int64_t vocab_start, int64_t shard_rows,
+                                               int ids_dtype, int grad_dtype, int main_grad_dtype) {
+    if (num_tokens < EWG_MIN_TOKENS || num_tokens > EWG_MAX_TOKENS) return 0;
+    if (hidden < 1 || hidden > kMaxHidden || vocab_start < 0 || shard_rows < 1) return 0;
+    if (!is_index_dtype(ids_dtype) || !is_float_dtype(grad_dtype) || !is_float_dtype(main_grad_dtype))
+        return 0;
+    // (shard_rows << pb) | (num_tokens - 1) < 2^31: one id bit more than the unsharded check
+    const int pb = ewg_position_bits(num_tokens);
+    if (shard_rows >= (int64_t(1) << (31 - pb))) return 0;
+    return 1;
+}
+
+int accumulate_embedding_wgrad_vocab_shard(const void *ids, const void *grad, void *main_grad,
+                                           int64_t num_tokens, int64_t hidden,
+                                           int64_t vocab_start, int64_t shard_rows,
+                                           int64_t grad_row_stride, int64_t main_grad_row_stride,
+                                           int ids_dtype, int grad_dtype, int main_grad_dtype,
+                                           void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, shard_rows, vocab_start, true,
+                      grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                      main_grad_dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,

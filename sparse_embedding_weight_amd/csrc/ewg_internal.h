@@ -111,9 +111,12 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
 // The whole accumulation in one kernel: sort, chunk sums over the grad rows,
 // single-chunk runs finished, ordered combine of long runs. One workgroup per
 // compute unit. grad_bf16 / mg_bf16 select the element types; vec selects
-// 16-byte rows.
+// 16-byte rows. Row v of main_grad belongs to id id_base + v, for v below
+// num_embeddings; with skip_outside other ids are left out, else they are
+// invalid (the call then touches nothing and reports them).
 hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
-                             const void *ids, int n, int num_embeddings, int pos_bits, int id_bits,
+                             const void *ids, int n, int num_embeddings, int64_t id_base,
+                             bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
                              int num_cus, uint32_t epoch, hipStream_t stream);

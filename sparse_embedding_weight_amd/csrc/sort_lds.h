@@ -39,6 +39,7 @@ struct SortSmem {
     uint32_t aux[kSortWaves << kMaxDigitBits];  // radix counters, then run starts
     uint64_t scan[kSortWaves + 1];
     int bad;
+    int n_keys;                                 // keys of ids inside the table (sorted first)
     int n_chunks, n_long, n_long_chunks, n_runs;
 };
 
@@ -92,13 +93,20 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t *s
 
 // Load the ids and build the keys in position order: wave w holds slots
 // [w*512, w*512 + 512) as 8 groups of 64; slots past n hold 0xffffffff, which
-// every pass ranks last. Returns the number of ids outside [0, num_embeddings)
-// (the same value in every thread).
+// every pass ranks last. The key of position s holds id - id_base, for ids in
+// [id_base, id_base + num_embeddings). With skip_outside, any other id is
+// left out: its slot holds 0xffffffff too (the id bits of a kept key are never
+// all ones, so kept keys rank first) and sm.n_keys counts the kept ones.
+// Otherwise an id outside is invalid: the number of those is returned (the
+// same value in every thread), and n_keys is n.
 template <typename IdT>
 __device__ __forceinline__ int load_keys(SortSmem &sm, const IdT *__restrict__ ids, int n, int num_embeddings,
-                         int pos_bits) {
+                         int pos_bits, int64_t id_base, bool skip_outside) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) sm.bad = 0;
+    if (tid == 0) {
+        sm.bad = 0;
+        sm.n_keys = 0;
+    }
     int64_t id[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {   // unconditional loads: all 8 in flight
@@ -106,22 +114,27 @@ __device__ __forceinline__ int load_keys(SortSmem &sm, const IdT *__restrict__ i
         id[i] = (int64_t)ids[s < n ? s : n - 1];
     }
     __syncthreads();
-    int bad = 0;
+    int bad = 0, kept = 0;
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int s = wave * kWaveSlots + i * 64 + lane;
         uint32_t key = 0xffffffffu;
         if (s < n) {
-            if (id[i] < 0 || id[i] >= num_embeddings) {
-                ++bad;
-                key = 0;
+            const int64_t v = id[i] - id_base;
+            if (v < 0 || v >= num_embeddings) {
+                if (!skip_outside) {
+                    ++bad;
+                    key = 0;
+                }
             } else {
-                key = ((uint32_t)id[i] << pos_bits) | (uint32_t)s;
+                key = ((uint32_t)v << pos_bits) | (uint32_t)s;
+                ++kept;
             }
         }
         sm.keys[0][s] = key;
     }
     if (bad) atomicAdd(&sm.bad, bad);
+    if (kept) atomicAdd(&sm.n_keys, kept);
     __syncthreads();
     return sm.bad;
 }

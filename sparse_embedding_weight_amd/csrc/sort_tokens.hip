@@ -16,7 +16,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_tokens_kernel(
     WsHeader *__restrict__ hdr, SortTables tables) {
     __shared__ SortSmem sm;
     const SortOutputs out = {tables, hdr, nullptr, nullptr};
-    const int bad = load_keys<IdT>(sm, ids, n, num_embeddings, pos_bits);
+    const int bad = load_keys<IdT>(sm, ids, n, num_embeddings, pos_bits, 0, false);
     if (bad) {
         report_invalid(out, bad);
         return;

@@ -122,3 +122,43 @@ def test_python_predicate_on_cpu_tensors_is_false():
     assert not ewg.can_accumulate_embedding_wgrad(ids, grad, mg)
     with pytest.raises(ValueError):
         ewg.accumulate_embedding_wgrad(ids, grad, mg)
+
+
+def test_vocab_shard_envelope_and_argument_errors():
+    can_s = B.lib.can_accumulate_embedding_wgrad_vocab_shard
+    # one id bit more than the unsharded test: rows < 2^(31 - position bits)
+    assert can_s(8192, 7168, 0, (1 << 18) - 1, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_s(8192, 7168, 0, 1 << 18, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert can_s(4096, 7168, 1 << 40, (1 << 19) - 1, B.EWG_INT64, B.EWG_FP32, B.EWG_BF16)
+    assert not can_s(8192, 7168, -1, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_s(8192, 7168, 0, 0, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_s(3072, 7168, 0, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_s(8192, 0, 0, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_s(8192, 7168, 0, 100, B.EWG_INT32, B.EWG_INT32, B.EWG_FP32)
+
+    def shard(**kw):
+        a = dict(ids=8, grad=16, main_grad=32, n=4096, h=64, start=1000, rows=100, gs=64, ms=64,
+                 i=B.EWG_INT32, g=B.EWG_BF16, m=B.EWG_FP32, ws=256 * 1024, wsb=1 << 30)
+        a.update(kw)
+        return B.lib.accumulate_embedding_wgrad_vocab_shard(
+            a["ids"], a["grad"], a["main_grad"], a["n"], a["h"], a["start"], a["rows"], a["gs"],
+            a["ms"], a["i"], a["g"], a["m"], a["ws"], a["wsb"], None)
+
+    # every case fails a host check, so nothing touches a device
+    assert shard(start=-5) == B.EWG_UNSUPPORTED
+    assert shard(rows=0) == B.EWG_UNSUPPORTED
+    assert shard(n=8192, rows=1 << 18) == B.EWG_UNSUPPORTED
+    assert shard(i=9) == B.EWG_INVALID_ARGUMENT
+    assert shard(ids=None) == B.EWG_INVALID_ARGUMENT
+    assert shard(gs=10) == B.EWG_INVALID_ARGUMENT
+    assert shard(ws=256 * 1024 + 4) == B.EWG_INVALID_ARGUMENT
+    assert shard(wsb=ewg.workspace_bytes(4096, 64) - 1) == B.EWG_WORKSPACE_TOO_SMALL
+
+
+def test_vocab_shard_python_predicate():
+    ids = torch.zeros(4096, dtype=torch.int32)
+    grad = torch.zeros(4096, 8, dtype=torch.bfloat16)
+    mg = torch.zeros(10, 8, dtype=torch.float32)
+    assert not ewg.can_accumulate_embedding_wgrad_vocab_shard(ids, grad, mg, 0)   # CPU tensors
+    with pytest.raises(ValueError):
+        ewg.accumulate_embedding_wgrad_vocab_shard(ids, grad, mg, 0)

@@ -313,3 +313,75 @@ def test_sort_tables_edge_ids():
         want = oracle.sort_tokens(ids_np)
         for k in want:
             assert np.array_equal(got[k].cpu().numpy().astype(np.int64), want[k]), k
+
+
+# ---- vocabulary shards: each shard's rows equal the unsharded result, bit for bit ----
+
+def _shard_calls(ids, grad, mg, bounds, ws=None):
+    """Run the shard entry point once per [bounds[k], bounds[k+1]) on views of mg."""
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        if hi > lo:
+            ewg.accumulate_embedding_wgrad_vocab_shard(ids, grad, mg[lo:hi], lo, workspace=ws)
+    torch.cuda.synchronize()
+
+
+def _check_against_oracle(ids, grad, before, after):
+    m_dt = "bf16" if after.dtype == torch.bfloat16 else "fp32"
+    rows = torch.unique(ids.reshape(-1).long())
+    got = wl.to_numpy_bits(after[rows].cpu())
+    want = oracle_rows(ids, grad, rows, before[rows].clone())
+    nan_g, nan_w = _is_nan_bits(got, m_dt), _is_nan_bits(want, m_dt)
+    assert np.array_equal(nan_g, nan_w)
+    gv = got.view(np.uint16 if m_dt == "bf16" else np.uint32)
+    wv = want.view(np.uint16 if m_dt == "bf16" else np.uint32)
+    assert int(((gv != wv) & ~nan_g).sum()) == 0
+    changed = (_bits(after) != _bits(before)).any(dim=1)
+    touched = torch.zeros(after.shape[0], dtype=torch.bool, device=after.device)
+    touched[rows] = True
+    assert not (changed & ~touched).any(), "a row whose id does not occur was written"
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_vocab_shards_equal_unsharded(name):
+    """Three shards of uneven size cover the vocabulary; together they give the
+    unsharded result (the oracle's) on every touched row and leave the rest."""
+    w = wl.WORKLOADS[name]
+    print(f"[shard parity] workload {name}", flush=True)
+    ids = torch.from_numpy(wl.make_ids(w)).cuda()
+    grad = wl.make_grad(w).cuda()
+    mg = wl.make_main_grad(w, "cuda")
+    before = mg.clone()
+    v = w.vocab
+    bounds = [0, v // 7 + 3, (5 * v) // 8, v]
+    _shard_calls(ids, grad, mg, bounds, ws=shared_workspace(ids.numel(), w.hidden))
+    _check_against_oracle(ids, grad, before, mg)
+
+
+def test_vocab_shard_edges():
+    """Shards with no id, a shard of a single row, a power-of-two shard whose last row
+    is used (the extra id bit), int64 ids far above 2^32, and the hottest id alone."""
+    rng = np.random.default_rng(71)
+    n, hidden = 4097, 136
+    base = 1 << 40
+    ids_np = rng.integers(0, 1 << 16, size=n)
+    ids_np[rng.choice(n, 900, replace=False)] = (1 << 16) - 1      # hot id on the last row
+    ids_np[:5] = 3                                                  # a run of 5 on row 3
+    ids_t = torch.from_numpy(ids_np + base).to(torch.int64).cuda()
+    grad = wl.normal_tensor(rng, (n, hidden), 0.01, "bf16").cuda()
+    mg = wl.normal_tensor(rng, (1 << 16, hidden), 1e-3, "fp32").cuda()
+    before = mg.clone()
+    ws = ewg.new_workspace(n, hidden, "cuda")
+    # an empty shard above every id, then a power-of-two shard of all rows
+    empty = torch.zeros(10, hidden, dtype=torch.float32, device="cuda")
+    ewg.accumulate_embedding_wgrad_vocab_shard(ids_t, grad, empty, base + (1 << 16), workspace=ws)
+    ewg.accumulate_embedding_wgrad_vocab_shard(ids_t, grad, mg, base, workspace=ws)
+    torch.cuda.synchronize()
+    assert not empty.any()
+    _check_against_oracle(ids_t - base, grad, before, mg)
+    # the same result from single-row shards around the run and the hot id
+    mg2 = before.clone()
+    bounds = [0, 3, 4, (1 << 16) - 1, 1 << 16]
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        ewg.accumulate_embedding_wgrad_vocab_shard(ids_t, grad, mg2[lo:hi], base + lo, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(mg2), _bits(mg))
