@@ -96,14 +96,19 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
  * accumulate_embedding_wgrad_sort_tokens need for these sizes (host only).
  * The workspace holds the chunk records and the fp32 partial sums of runs
  * longer than EWG_NROWS rows, and the counters the kernel's workgroups share;
- * its content between calls is not part of the interface except for two
- * int32 words: the first 4 bytes (see below) and the one at byte offset
+ * its content between calls is not part of the interface except for three
+ * int32 words: the first 4 bytes (see below); the one at byte offset
  * EWG_WS_WAIT_TIMEOUTS_OFFSET, which counts the bounded waits inside the
  * kernel that gave up since the workspace was zero-filled (a diagnostic: no
- * wait is expected to give up; when one does, the call's result is wrong).
+ * wait is expected to give up; when one does, the call's result is wrong);
+ * and the one at EWG_WS_STOLEN_SHARES_OFFSET, the number of shares of
+ * long-run work that the last call's waiting workgroups took over from
+ * workgroups that had not started (a diagnostic: 0 when all of the launch's
+ * workgroups run together, and the result is the same either way).
  * 0 if the sizes are out of range.
  */
 #define EWG_WS_WAIT_TIMEOUTS_OFFSET 132
+#define EWG_WS_STOLEN_SHARES_OFFSET 148
 
 size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);
 
@@ -136,11 +141,12 @@ size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hi
  * other workgroups finish every run of at most EWG_NROWS rows; then all of
  * them sum the chunks of the long runs and add those sums in chunk order.
  * Workgroups hand work to each other through the workspace, and every wait in
- * the kernel is bounded; the waits end in time when the launch's workgroups
- * run together (one per compute unit: the stream must not be restricted to
- * fewer compute units). A wait that gives up is counted in the workspace's
- * int32 at EWG_WS_WAIT_TIMEOUTS_OFFSET and its work is skipped. Any alignment
- * is accepted; 16-byte aligned rows take the vector path.
+ * the kernel is bounded. A workgroup that waits long for long-run work of
+ * workgroups that have not started (other work holding compute units) takes
+ * that work over, so the call needs no particular number of workgroups
+ * running at once. A wait that gives up is counted in the workspace's int32
+ * at EWG_WS_WAIT_TIMEOUTS_OFFSET and its work is skipped. Any alignment is
+ * accepted; 16-byte aligned rows take the vector path.
  *
  * The workspace carries counters from one call to the next: a call that did
  * not run to completion (for example a device fault) leaves it unusable

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     new_workspace,
     position_bits,
     sort_tokens,
+    stolen_shares,
     wait_timeouts,
     workspace_bytes,
 )

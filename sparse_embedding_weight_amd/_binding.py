@@ -264,6 +264,14 @@ def invalid_id_count(workspace: torch.Tensor) -> int:
 
 
 WS_WAIT_TIMEOUTS_OFFSET = 132   # EWG_WS_WAIT_TIMEOUTS_OFFSET
+WS_STOLEN_SHARES_OFFSET = 148   # EWG_WS_STOLEN_SHARES_OFFSET
+
+
+def stolen_shares(workspace: torch.Tensor) -> int:
+    """Shares of long-run work that the last call's waiting workgroups took over
+    from workgroups that had not started (diagnostic word; synchronises)."""
+    o = WS_STOLEN_SHARES_OFFSET
+    return int(workspace[o:o + 4].view(torch.int32).item())
 
 
 def wait_timeouts(workspace: torch.Tensor) -> int:

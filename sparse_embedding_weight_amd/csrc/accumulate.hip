@@ -56,6 +56,8 @@ namespace {
 
 constexpr int kTilesPerUnit = 4;         // most column tiles of one chunk per unit / batch of loads
 constexpr int64_t kWaitLimit = 1 << 22;  // polls before a wait gives up (seconds)
+constexpr uint64_t kStealAfterTicks = 20000;   // 200 us of the 100 MHz clock: a combine task
+                                               // then takes the run's unclaimed long shares
 constexpr int kHashSlots = 16384;        // > 2 x kMaxTokens: linear probing always ends
 constexpr int kHashBits = 14;
 constexpr int kOwnedMax = 256;           // short runs gathered per round by one follower
@@ -90,6 +92,7 @@ struct LongSmem {
     u32x4 rec[2 * kMaxLongChunks];      // unit records of this workgroup's chunks, two halves each
     uint32_t run_cnt[kMaxLongRuns];     // units of each long run this workgroup has finished
     uint32_t claim;                     // next unit of this workgroup's share to claim
+    uint32_t won;                       // the share's slot was claimed by this workgroup
 };
 
 union AccSmem {
@@ -514,7 +517,8 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
                                                int hidden, WsHeader *__restrict__ hdr,
                                                __amdgpu_buffer_rsrc_t units_rs,
                                                __amdgpu_buffer_rsrc_t runs_rs,
-                                               uint32_t *__restrict__ done, uint32_t epoch) {
+                                               uint32_t *__restrict__ done,
+                                               uint32_t *__restrict__ shares, uint32_t epoch) {
     const int tid = threadIdx.x;
     uint32_t n_lc = 0, n_lr = 0, n_tasks = 0;
     const SortOutputs out0 = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
@@ -579,10 +583,13 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
         n_tasks = (uint32_t)total;
 
     }
+    // every share of long units unclaimed (they are claimed only after the flag)
+    for (int i = tid; i < (int)gridDim.x; i += kSortThreads) store_coherent(&shares[i], 0u);
     if (tid == 0) {
         store_coherent(&hdr->pub_long_chunks, n_lc);
         store_coherent(&hdr->pub_long_runs, n_lr);
         store_coherent(&hdr->pub_tasks, n_tasks);
+        store_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 0u);
         store_coherent(&hdr->task_ticket, 0u);
     }
     // every store of every wave has completed, then the flag goes up
@@ -606,6 +613,19 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     return true;
 }
 
+// First long unit of share w of the launch's gridDim.x shares of `total`.
+__device__ __forceinline__ uint32_t share_begin(uint32_t total, uint32_t w) {
+    return (uint32_t)((uint64_t)total * w / gridDim.x);
+}
+
+// The share that holds unit u (< total).
+__device__ __forceinline__ uint32_t share_of(uint32_t total, uint32_t u) {
+    uint32_t w = (uint32_t)(((uint64_t)u * gridDim.x) / total);
+    while (w + 1 < gridDim.x && share_begin(total, w + 1) <= u) ++w;
+    while (w > 0 && share_begin(total, w) > u) --w;
+    return w;
+}
+
 // Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
 // takes units [w * U / W, (w + 1) * U / W) of the U = chunks * tiles units:
 // the shares are fixed by the published chunk count alone, so no device-wide
@@ -617,7 +637,8 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
 // in LDS and added to the run's counter of this workgroup's group once,
 // after all stores of the workgroup have completed.
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ void long_units(LongSmem &ls, WsHeader *__restrict__ hdr,
+__device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t share, uint32_t mark,
+                                           uint32_t *__restrict__ shares, WsHeader *__restrict__ hdr,
                                            __amdgpu_buffer_rsrc_t units_rs,
                                            uint32_t *__restrict__ done, uint32_t n_lc,
                                            uint32_t n_lr, int n,
@@ -628,15 +649,27 @@ __device__ __forceinline__ void long_units(LongSmem &ls, WsHeader *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63;
     const int full_tiles = hidden / (64 * VEC);
     const uint32_t total = n_lc * (uint32_t)tiles;
-    const uint32_t lo = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
-    const uint32_t hi = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
+    const uint32_t lo = share_begin(total, share);
+    const uint32_t hi = share_begin(total, share + 1);
     const uint32_t c_lo = lo / (uint32_t)tiles;
     const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;   // chunks [c_lo, c_hi)
+    // claim the share (its slot from 0 to `mark`: 1 for the owner, 2 for another
+    // workgroup) while its records are fetched; both round trips overlap
+    bool won = true;
+    if (tid == 0) {
+        uint32_t expected = 0u;
+        won = __hip_atomic_compare_exchange_strong(&shares[share], &expected, mark, __ATOMIC_RELAXED,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     for (uint32_t i = (uint32_t)tid; i < 2 * (c_hi - c_lo); i += kSortThreads)
         ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
     for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) ls.run_cnt[r] = 0u;
-    if (tid == 0) ls.claim = 0u;
+    if (tid == 0) {
+        ls.claim = 0u;
+        ls.won = won ? 1u : 0u;
+    }
     __syncthreads();
+    if (!ls.won) return false;   // uniform: the share is someone else's
 
     // every branch below is on a wave-uniform value; the single-lane LDS
     // updates are whole-wave atomics in which only lane 0 adds anything
@@ -677,21 +710,26 @@ __device__ __forceinline__ void long_units(LongSmem &ls, WsHeader *__restrict__ 
         const uint32_t m = ls.run_cnt[r];
         if (m) fetch_add_coherent(&done[((size_t)r * kDoneGroups + grp) * kDoneStride], m);
     }
+    return true;
 }
 
 // ---- phase 4: ordered combine of long runs -------------------------------------
 
-template <typename G, typename M>
-__device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
+template <typename G, typename M, int VEC>
+__device__ __forceinline__ void combine_tasks(AccSmem &sm, uint32_t *s_word,
                                               WsHeader *__restrict__ hdr,
+                                              __amdgpu_buffer_rsrc_t units_rs,
                                               __amdgpu_buffer_rsrc_t runs_rs,
                                               uint32_t *__restrict__ done,
-                                              const float *__restrict__ partial,
+                                              uint32_t *__restrict__ shares, bool flag_seen,
+                                              int n, const typename G::T *__restrict__ grad,
+                                              int64_t grad_stride, float *__restrict__ partial,
                                               int64_t partial_stride,
                                               typename M::T *__restrict__ main_grad,
                                               int64_t mg_stride, int hidden, int tiles,
                                               int num_embeddings, uint32_t n_lc_max,
-                                              uint32_t n_lr_max) {
+                                              uint32_t n_lr_max, uint32_t epoch) {
+    CombineSmem &cs = sm.comb;
     using MT = typename M::T;
     const int tid = threadIdx.x;
     if (tid == 0) {
@@ -703,6 +741,8 @@ __device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
     const int n_lr = (int)s_word[0];
     const uint32_t n_tasks = s_word[1];
     if (n_lr == 0 || n_tasks == 0) return;   // uniform
+    const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
+    const uint32_t total = n_lc * (uint32_t)tiles;
     for (int r = tid; r < n_lr; r += kSortThreads) cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
     __syncthreads();
 
@@ -730,25 +770,60 @@ __device__ __forceinline__ void combine_tasks(CombineSmem &cs, uint32_t *s_word,
         // a record that does not describe this call's work is skipped
         const bool valid = rec.w <= t && row < (uint32_t)num_embeddings && chunks >= 1 &&
                            first < n_lc_max && chunks <= n_lc_max - first && col0 < hidden;
-        if (tid == 0) {
-            int ok = valid ? 1 : 0;
-            const uint32_t target = chunks * (uint32_t)tiles;
-            int64_t spins = 0;
-            for (;;) {
-                uint32_t sum = 0;
-                for (int g = 0; g < kDoneGroups; ++g)
-                    sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
-                if (!ok || sum >= target) break;
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kWaitLimit) {
-                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-                    ok = 0;
+        // Wait until the run's units are all counted. If that takes long, some
+        // workgroups of the launch are not running (more were launched than fit,
+        // or other work holds compute units): then this workgroup processes the
+        // run's shares that nobody has taken yet itself, and waits again.
+        int64_t spins = 0;
+        bool task_ok = false;
+        // stealing needs the run's units inside this call's unit list
+        const bool can_steal = flag_seen && valid && first + chunks <= n_lc;
+        for (;;) {
+            if (tid == 0) {
+                uint32_t status = valid ? 0u : 3u;   // 0 waiting, 1 done, 2 steal, 3 give up
+                const uint32_t target = chunks * (uint32_t)tiles;
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                while (status == 0u) {
+                    uint32_t sum = 0;
+                    for (int g = 0; g < kDoneGroups; ++g)
+                        sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
+                    if (sum >= target) {
+                        status = 1u;
+                    } else if (++spins > kWaitLimit) {
+                        fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+                        status = 3u;
+                    } else if (can_steal && __builtin_amdgcn_s_memrealtime() - t0 > kStealAfterTicks) {
+                        status = 2u;
+                    } else {
+                        __builtin_amdgcn_s_sleep(2);
+                    }
                 }
+                s_word[3] = status;
             }
-            s_word[3] = (uint32_t)ok;
+            __syncthreads();
+            const uint32_t status = s_word[3];
+            if (status != 2u) {
+                task_ok = status == 1u;
+                break;
+            }
+            // the run's units are [first * tiles, (first + chunks) * tiles)
+            const uint32_t w_first = share_of(total, first * (uint32_t)tiles);
+            const uint32_t w_last = share_of(total, (first + chunks) * (uint32_t)tiles - 1u);   // < gridDim.x
+            for (uint32_t w = w_first; w <= w_last; ++w) {
+                if (long_units<G, M, VEC>(sm.lng, w, 2u, shares, hdr, units_rs, done, n_lc,
+                                          (uint32_t)n_lr, n, grad, grad_stride, partial,
+                                          partial_stride, hidden, tiles, epoch) &&
+                    tid == 0)
+                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);
+                __syncthreads();
+            }
+            __syncthreads();   // the long units used the LDS of the run list: load it again
+            for (int r = tid; r < n_lr; r += kSortThreads)
+                cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
+            __syncthreads();
         }
         __syncthreads();
-        if (s_word[3]) {   // uniform
+        if (task_ok) {   // uniform
             const int wc = (int)(hidden - col0 < wdt ? hidden - col0 : wdt);
             MT *mrow = main_grad + (int64_t)row * mg_stride + col0;
             constexpr int kCols = kMaxCombineCols / kSortThreads;   // columns per thread
@@ -836,8 +911,8 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     const typename G::T *__restrict__ grad, int64_t grad_stride,
     typename M::T *__restrict__ main_grad, int64_t mg_stride, int hidden, int tiles,
     WsHeader *__restrict__ hdr, uint8_t *__restrict__ units,
-    uint8_t *__restrict__ runs, uint32_t *__restrict__ done, float *__restrict__ partial,
-    int64_t partial_stride, uint32_t epoch) {
+    uint8_t *__restrict__ runs, uint32_t *__restrict__ done, uint32_t *__restrict__ shares,
+    float *__restrict__ partial, int64_t partial_stride, uint32_t epoch, int defer_odd_shares) {
     __shared__ AccSmem sm;
     __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
     const int tid = threadIdx.x;
@@ -850,7 +925,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     if (blockIdx.x == 0) {
         leader_publish<IdT>(sm.sort, ids, n, num_embeddings, id_base, skip_outside != 0, pos_bits,
                             id_bits, hidden, hdr,
-                            units_rs, runs_rs, done, epoch);
+                            units_rs, runs_rs, done, shares, epoch);
     } else {
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
                                             skip_outside != 0, grad, grad_stride,
@@ -864,12 +939,18 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     if (s_word[0] == 0u) {   // uniform: every wave saw the flag
         const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
         const uint32_t n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
-        long_units<G, M, VEC>(sm.lng, hdr, units_rs, done, n_lc, n_lr, n, grad, grad_stride,
-                              partial, partial_stride, hidden, tiles, epoch);
+        // this workgroup's own share, unless a waiting combine task took it already
+        // (a test setting leaves every other share to the combine tasks)
+        if (!(defer_odd_shares && (blockIdx.x & 1u)))
+            long_units<G, M, VEC>(sm.lng, blockIdx.x, 1u, shares, hdr, units_rs, done, n_lc, n_lr,
+                                  n, grad, grad_stride, partial, partial_stride, hidden, tiles,
+                                  epoch);
     }
+    const bool flag_seen = s_word[0] == 0u;
     __syncthreads();
-    combine_tasks<G, M>(sm.comb, s_word, hdr, runs_rs, done, partial, partial_stride, main_grad,
-                        mg_stride, hidden, tiles, num_embeddings, n_lc_max, n_lr_max);
+    combine_tasks<G, M, VEC>(sm, s_word, hdr, units_rs, runs_rs, done, shares, flag_seen, n, grad,
+                             grad_stride, partial, partial_stride, main_grad, mg_stride, hidden,
+                             tiles, num_embeddings, n_lc_max, n_lr_max, epoch);
 
     // ---- phase 5: the last workgroup out resets the call's shared state ----
     // two levels of counters, so that no address takes more than ~32 atomics
@@ -897,7 +978,7 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, i
                   int pos_bits, int id_bits,
                   const void *grad, int64_t grad_stride, void *main_grad, int64_t mg_stride,
                   int hidden, void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                  hipStream_t stream) {
+                  int defer_odd_shares, hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     const int tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
     const int grid = num_cus < 2 ? 2 : (num_cus > kMaxGrid ? kMaxGrid : num_cus);
@@ -906,8 +987,8 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, i
         static_cast<const typename G::T *>(grad), grad_stride,
         static_cast<typename M::T *>(main_grad), mg_stride, hidden, tiles,
         reinterpret_cast<WsHeader *>(ws), reinterpret_cast<uint8_t *>(ws + l.units), reinterpret_cast<uint8_t *>(ws + l.runs),
-        reinterpret_cast<uint32_t *>(ws + l.done), reinterpret_cast<float *>(ws + l.partial),
-        l.partial_stride, epoch);
+        reinterpret_cast<uint32_t *>(ws + l.done), reinterpret_cast<uint32_t *>(ws + l.shares),
+        reinterpret_cast<float *>(ws + l.partial), l.partial_stride, epoch, defer_odd_shares);
     return hipGetLastError();
 }
 
@@ -917,11 +998,11 @@ hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *id
                           int id_bits, const void *grad,
                           int64_t grad_stride, void *main_grad, int64_t mg_stride, int hidden,
                           void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                          hipStream_t stream) {
+                          int defer_odd_shares, hipStream_t stream) {
 #define EWG_ACC(G, M, V)                                                                        \
     launch<IdT, G, M, V>(ids, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits, grad,   \
                          grad_stride, main_grad,                                                  \
-                         mg_stride, hidden, workspace, l, num_cus, epoch, stream)
+                         mg_stride, hidden, workspace, l, num_cus, epoch, defer_odd_shares, stream)
     if (grad_bf16) {
         if (mg_bf16) return vec ? EWG_ACC(BF16, BF16, 8) : EWG_ACC(BF16, BF16, 1);
         return vec ? EWG_ACC(BF16, F32, 8) : EWG_ACC(BF16, F32, 1);
@@ -938,14 +1019,15 @@ hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool 
                              bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
-                             int num_cus, uint32_t epoch, hipStream_t stream) {
+                             int num_cus, uint32_t epoch, int defer_odd_shares,
+                             hipStream_t stream) {
     if (ids_int64)
         return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
                                        skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
-                                       workspace, l, num_cus, epoch, stream);
+                                       workspace, l, num_cus, epoch, defer_odd_shares, stream);
     return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
                                    skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
-                                   workspace, l, num_cus, epoch, stream);
+                                   workspace, l, num_cus, epoch, defer_odd_shares, stream);
 }
 
 }  // namespace ewg

@@ -6,6 +6,8 @@
 
 #include <atomic>
 
+#include <cstdlib>
+
 #include "ewg_internal.h"
 
 namespace {
@@ -31,6 +33,26 @@ size_t float_size(int d) { return d == EWG_BF16 ? 2 : 4; }
 
 bool aligned(const void *p, int64_t row_stride_bytes, size_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a == 0) && (row_stride_bytes % (int64_t)a == 0);
+}
+
+// Workgroups of one launch: one per compute unit. The environment variable
+// EWG_GRID (2..4095) overrides it; the tests use that to run launches with
+// far fewer workgroups (long shares and many rounds per workgroup) and with
+// more than fit at once (combine tasks that take the long shares of
+// workgroups that have not started).
+int launch_grid(int cus) {
+    if (const char *e = getenv("EWG_GRID")) {
+        const long g = strtol(e, nullptr, 10);
+        if (g >= 2 && g <= kMaxGrid) return (int)g;
+    }
+    return cus;
+}
+
+// EWG_DEFER_ODD_SHARES=1 (tests only): the workgroups of odd number leave
+// their long shares to the combine tasks, which then take them over.
+int defer_odd_shares() {
+    const char *e = getenv("EWG_DEFER_ODD_SHARES");
+    return e && e[0] == '1' ? 1 : 0;
 }
 
 // Compute units of the current device, cached per device ordinal.
@@ -123,7 +145,8 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                                      (int)num_embeddings, id_base, shard, pos_bits, id_bits, grad,
                                      grad_row_stride,
                                      main_grad, main_grad_row_stride, (int)hidden, workspace, l,
-                                     num_cus(), next_epoch(), stream));
+                                     launch_grid(num_cus()), next_epoch(), defer_odd_shares(),
+                                     stream));
     if (st != EWG_OK) return st;
     if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
     return EWG_OK;

@@ -41,7 +41,8 @@ struct WsHeader {
     uint32_t pub_long_chunks; // long chunks of this call
     uint32_t pub_long_runs;   // long runs of this call
     uint32_t pub_tasks;       // combine tasks of this call
-    int32_t pad1[27];
+    int32_t stolen_shares;    // long shares a waiting combine task took over in the last call
+    int32_t pad1[26];
     // line 2: next combine task to hand out
     uint32_t task_ticket;
     int32_t pad2[31];
@@ -53,6 +54,8 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
 static_assert(offsetof(WsHeader, wait_timeouts) == EWG_WS_WAIT_TIMEOUTS_OFFSET,
+              "documented diagnostic word");
+static_assert(offsetof(WsHeader, stolen_shares) == EWG_WS_STOLEN_SHARES_OFFSET,
               "documented diagnostic word");
 
 // Optional outputs of the sort step (all null in the accumulate path).
@@ -67,6 +70,8 @@ struct SortTables {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr int kMaxGrid = 4095;       // workgroups of one launch, at most
+
 // Byte offsets inside the workspace for num_tokens tokens and `hidden` columns.
 // The header has a fixed place; everything after it depends on the sizes and
 // is written by a call before that call reads it.
@@ -74,6 +79,7 @@ struct WsLayout {
     size_t units;            // 32-byte record per long chunk (positions, rows, run)
     size_t runs;             // 16-byte record per long run (row, first chunk, chunks, tasks)
     size_t done;             // per long run: finished units, kDoneGroups counters of 128 bytes
+    size_t shares;           // per workgroup of the launch: who processes its long share
     size_t partial;          // float[max_long_chunks][partial_stride]
     size_t total;
     int64_t partial_stride;  // floats per partial row
@@ -81,7 +87,6 @@ struct WsLayout {
     int64_t max_long_runs;   // a long run has at least 11 rows
 };
 
-constexpr int kMaxGrid = 4095;       // workgroups of one launch, at most
 constexpr size_t kUnitRecordBytes = 32;
 constexpr size_t kRunRecordBytes = 16;
 constexpr size_t kDoneStride = 32;   // uint32 words between two unit counters (128 bytes)
@@ -94,7 +99,8 @@ inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     l.units = sizeof(WsHeader);
     l.runs = round_up(l.units + kUnitRecordBytes * (size_t)(l.max_long_chunks + 1), 256);
     l.done = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
-    l.partial = round_up(l.done + 4 * kDoneStride * kDoneGroups * (size_t)(l.max_long_runs + 1), 256);
+    l.shares = round_up(l.done + 4 * kDoneStride * kDoneGroups * (size_t)(l.max_long_runs + 1), 256);
+    l.partial = round_up(l.shares + 4 * (size_t)kMaxGrid, 256);
     l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
     l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
                                        (size_t)l.max_long_chunks, 256);
@@ -113,12 +119,14 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
 // compute unit. grad_bf16 / mg_bf16 select the element types; vec selects
 // 16-byte rows. Row v of main_grad belongs to id id_base + v, for v below
 // num_embeddings; with skip_outside other ids are left out, else they are
-// invalid (the call then touches nothing and reports them).
+// invalid (the call then touches nothing and reports them). defer_odd_shares
+// (tests only) leaves the long shares of odd workgroups to the combine tasks.
 hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
                              const void *ids, int n, int num_embeddings, int64_t id_base,
                              bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
-                             int num_cus, uint32_t epoch, hipStream_t stream);
+                             int num_cus, uint32_t epoch, int defer_odd_shares,
+                             hipStream_t stream);
 
 }  // namespace ewg

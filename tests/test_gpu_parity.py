@@ -385,3 +385,43 @@ def test_vocab_shard_edges():
         ewg.accumulate_embedding_wgrad_vocab_shard(ids_t, grad, mg2[lo:hi], base + lo, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(_bits(mg2), _bits(mg))
+
+
+# ---- launch sizes: few workgroups (long shares, many rounds) and more than fit at once ----
+
+@pytest.mark.parametrize("grid", ["2", "3", "16", "2x", "3x"])
+@pytest.mark.parametrize("name", ["zipf1.1_4096_v32000_h4096", "longrun_8192_v129280_h7168"])
+def test_launch_sizes(grid, name, monkeypatch):
+    """EWG_GRID sets the workgroups of a launch. With 2, 3 or 16 one follower
+    handles many rounds of short runs and a long share of many chunks; with two or
+    three times the compute units, workgroups that have not started hold long
+    shares that waiting combine tasks take over. The result stays bit-exact and
+    no bounded wait gives up."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = int(grid[:-1]) * cus if grid.endswith("x") else int(grid)
+    monkeypatch.setenv("EWG_GRID", str(g))
+    w = wl.WORKLOADS[name]
+    print(f"[launch size] {name} grid {g}", flush=True)
+    ids = torch.from_numpy(wl.make_ids(w)).cuda()
+    grad = wl.make_grad(w).cuda()
+    mg = wl.make_main_grad(w, "cuda")
+    ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
+    check_call(ids, grad, mg, workspace=ws)
+
+
+@pytest.mark.parametrize("name", ["zipf1.1_8192_v129280_h7168", "longrun_8192_v129280_h7168",
+                                  "zipf1.3_4x2048_v129280_h7168_bf16mg"])
+def test_combine_takes_over_unclaimed_shares(name, monkeypatch):
+    """EWG_DEFER_ODD_SHARES makes every odd workgroup leave its long share
+    unclaimed, as a workgroup that cannot start would: the combine tasks that
+    wait for those units take the shares over after a while. Bit-exact, no wait
+    gives up, and the diagnostic word counts the shares taken over."""
+    monkeypatch.setenv("EWG_DEFER_ODD_SHARES", "1")
+    w = wl.WORKLOADS[name]
+    print(f"[taken-over shares] {name}", flush=True)
+    ids = torch.from_numpy(wl.make_ids(w)).cuda()
+    grad = wl.make_grad(w).cuda()
+    mg = wl.make_main_grad(w, "cuda")
+    ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
+    check_call(ids, grad, mg, workspace=ws)
+    assert ewg.stolen_shares(ws) > 0
