@@ -14,7 +14,7 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libembedding
 
 if not os.path.exists(LIBRARY):
     raise ImportError(
-        f"{LIBRARY} is missing: build it with `python -m sparse_embedding_weight_amd.build` "
+        f"{LIBRARY} is missing: build it with `python sparse_embedding_weight_amd/build.py` "
         "(or __graft_entry__.build()). There is no fallback path.")
 
 lib = ctypes.CDLL(LIBRARY)

@@ -1,6 +1,6 @@
 """Build libembedding_wgrad.so (HIP, gfx950) in place, next to this file.
 
-    python -m sparse_embedding_weight_amd.build
+    python sparse_embedding_weight_amd/build.py
 """
 import os
 import subprocess

@@ -584,7 +584,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
 
     }
     // every share of long units unclaimed (they are claimed only after the flag)
-    for (int i = tid; i < (int)gridDim.x; i += kSortThreads) store_coherent(&shares[i], 0u);
+    for (int i = tid; i < (int)gridDim.x; i += kSortThreads) store_coherent(&shares[(size_t)i * kDoneStride], 0u);
     if (tid == 0) {
         store_coherent(&hdr->pub_long_chunks, n_lc);
         store_coherent(&hdr->pub_long_runs, n_lr);
@@ -626,6 +626,16 @@ __device__ __forceinline__ uint32_t share_of(uint32_t total, uint32_t u) {
     return w;
 }
 
+// Share w's slot (128 bytes apart, zeroed by workgroup 0 before the flag) goes
+// from 0 to `mark` once: 1 when its own workgroup takes it, 2 when a waiting
+// combine task does. True if this call made that change.
+__device__ __forceinline__ bool claim_share(uint32_t *__restrict__ shares, uint32_t w, uint32_t mark) {
+    uint32_t expected = 0u;
+    return __hip_atomic_compare_exchange_strong(&shares[(size_t)w * kDoneStride], &expected, mark,
+                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
 // takes units [w * U / W, (w + 1) * U / W) of the U = chunks * tiles units:
 // the shares are fixed by the published chunk count alone, so no device-wide
@@ -653,14 +663,10 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t share, uint32_
     const uint32_t hi = share_begin(total, share + 1);
     const uint32_t c_lo = lo / (uint32_t)tiles;
     const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;   // chunks [c_lo, c_hi)
-    // claim the share (its slot from 0 to `mark`: 1 for the owner, 2 for another
-    // workgroup) while its records are fetched; both round trips overlap
+    // claim the share (its slot from 0 to `mark`) while its records are
+    // fetched, so that both round trips overlap; mark 0: the caller holds it
     bool won = true;
-    if (tid == 0) {
-        uint32_t expected = 0u;
-        won = __hip_atomic_compare_exchange_strong(&shares[share], &expected, mark, __ATOMIC_RELAXED,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0 && mark != 0u) won = claim_share(shares, share, mark);
     for (uint32_t i = (uint32_t)tid; i < 2 * (c_hi - c_lo); i += kSortThreads)
         ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
     for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) ls.run_cnt[r] = 0u;
@@ -715,20 +721,31 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t share, uint32_
 
 // ---- phase 4: ordered combine of long runs -------------------------------------
 
+// Where a workgroup stands in its combine tasks between two calls of
+// combine_tasks (the values are the same in every thread).
+struct CombineCursor {
+    uint32_t task;        // the task being waited for, if have_task
+    bool have_task;
+    int64_t spins;        // polls spent on that task's wait
+    uint32_t n_lc, n_lr;  // the published long-chunk and long-run counts
+};
+
+// Returns false once no combine task is left. Returns true, with the task
+// kept in the cursor, when the current task's run still needs the shares
+// [*w_lo, *w_hi) that no workgroup has taken: the caller takes and processes
+// them (long_units, which reuses this LDS) and calls again to resume the task.
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ void combine_tasks(AccSmem &sm, uint32_t *s_word,
+__device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, CombineCursor &cur,
+                                              uint32_t *w_lo, uint32_t *w_hi,
                                               WsHeader *__restrict__ hdr,
-                                              __amdgpu_buffer_rsrc_t units_rs,
                                               __amdgpu_buffer_rsrc_t runs_rs,
-                                              uint32_t *__restrict__ done,
-                                              uint32_t *__restrict__ shares, bool flag_seen,
-                                              int n, const typename G::T *__restrict__ grad,
-                                              int64_t grad_stride, float *__restrict__ partial,
+                                              uint32_t *__restrict__ done, bool flag_seen,
+                                              float *__restrict__ partial,
                                               int64_t partial_stride,
                                               typename M::T *__restrict__ main_grad,
                                               int64_t mg_stride, int hidden, int tiles,
                                               int num_embeddings, uint32_t n_lc_max,
-                                              uint32_t n_lr_max, uint32_t epoch) {
+                                              uint32_t n_lr_max) {
     CombineSmem &cs = sm.comb;
     using MT = typename M::T;
     const int tid = threadIdx.x;
@@ -740,23 +757,30 @@ __device__ __forceinline__ void combine_tasks(AccSmem &sm, uint32_t *s_word,
     __syncthreads();
     const int n_lr = (int)s_word[0];
     const uint32_t n_tasks = s_word[1];
-    if (n_lr == 0 || n_tasks == 0) return;   // uniform
+    if (n_lr == 0 || n_tasks == 0) return false;   // uniform
     const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
     const uint32_t total = n_lc * (uint32_t)tiles;
+    cur.n_lc = n_lc;
+    cur.n_lr = (uint32_t)n_lr;
     for (int r = tid; r < n_lr; r += kSortThreads) cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
     __syncthreads();
 
     for (;;) {
-        if (tid == 0) {
-            // a cheap look first: most late workgroups find the tasks gone
-            // without a serialised atomic
-            uint32_t t = load_coherent(&hdr->task_ticket);
-            if (t < n_tasks) t = fetch_add_coherent(&hdr->task_ticket, 1u);
-            s_word[2] = t;
+        if (!cur.have_task) {   // uniform
+            if (tid == 0) {
+                // a cheap look first: most late workgroups find the tasks gone
+                // without a serialised atomic
+                uint32_t t = load_coherent(&hdr->task_ticket);
+                if (t < n_tasks) t = fetch_add_coherent(&hdr->task_ticket, 1u);
+                s_word[2] = t;
+            }
+            __syncthreads();
+            cur.task = s_word[2];
+            cur.have_task = true;
+            cur.spins = 0;
         }
-        __syncthreads();
-        const uint32_t t = s_word[2];
-        if (t >= n_tasks) break;   // uniform
+        const uint32_t t = cur.task;
+        if (t >= n_tasks) return false;   // uniform
         // the run: the last one whose first task is at or before t
         int lo = 0, hi = n_lr;
         while (hi - lo > 1) {
@@ -772,56 +796,45 @@ __device__ __forceinline__ void combine_tasks(AccSmem &sm, uint32_t *s_word,
                            first < n_lc_max && chunks <= n_lc_max - first && col0 < hidden;
         // Wait until the run's units are all counted. If that takes long, some
         // workgroups of the launch are not running (more were launched than fit,
-        // or other work holds compute units): then this workgroup processes the
-        // run's shares that nobody has taken yet itself, and waits again.
-        int64_t spins = 0;
-        bool task_ok = false;
-        // stealing needs the run's units inside this call's unit list
+        // or other work holds compute units): then the caller processes the
+        // run's shares that nobody has taken yet, and the wait resumes.
+        // Stealing needs the run's units inside this call's unit list.
         const bool can_steal = flag_seen && valid && first + chunks <= n_lc;
-        for (;;) {
-            if (tid == 0) {
-                uint32_t status = valid ? 0u : 3u;   // 0 waiting, 1 done, 2 steal, 3 give up
-                const uint32_t target = chunks * (uint32_t)tiles;
-                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                while (status == 0u) {
-                    uint32_t sum = 0;
-                    for (int g = 0; g < kDoneGroups; ++g)
-                        sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
-                    if (sum >= target) {
-                        status = 1u;
-                    } else if (++spins > kWaitLimit) {
-                        fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-                        status = 3u;
-                    } else if (can_steal && __builtin_amdgcn_s_memrealtime() - t0 > kStealAfterTicks) {
-                        status = 2u;
-                    } else {
-                        __builtin_amdgcn_s_sleep(2);
-                    }
+        if (tid == 0) {
+            uint32_t status = valid ? 0u : 3u;   // 0 waiting, 1 done, 2 steal, 3 give up
+            const uint32_t target = chunks * (uint32_t)tiles;
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            int64_t spins = cur.spins;
+            while (status == 0u) {
+                uint32_t sum = 0;
+                for (int g = 0; g < kDoneGroups; ++g)
+                    sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
+                if (sum >= target) {
+                    status = 1u;
+                } else if (++spins > kWaitLimit) {
+                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+                    status = 3u;
+                } else if (can_steal && __builtin_amdgcn_s_memrealtime() - t0 > kStealAfterTicks) {
+                    status = 2u;
+                } else {
+                    __builtin_amdgcn_s_sleep(2);
                 }
-                s_word[3] = status;
             }
-            __syncthreads();
-            const uint32_t status = s_word[3];
-            if (status != 2u) {
-                task_ok = status == 1u;
-                break;
-            }
-            // the run's units are [first * tiles, (first + chunks) * tiles)
-            const uint32_t w_first = share_of(total, first * (uint32_t)tiles);
-            const uint32_t w_last = share_of(total, (first + chunks) * (uint32_t)tiles - 1u);   // < gridDim.x
-            for (uint32_t w = w_first; w <= w_last; ++w) {
-                if (long_units<G, M, VEC>(sm.lng, w, 2u, shares, hdr, units_rs, done, n_lc,
-                                          (uint32_t)n_lr, n, grad, grad_stride, partial,
-                                          partial_stride, hidden, tiles, epoch) &&
-                    tid == 0)
-                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);
-                __syncthreads();
-            }
-            __syncthreads();   // the long units used the LDS of the run list: load it again
-            for (int r = tid; r < n_lr; r += kSortThreads)
-                cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
-            __syncthreads();
+            s_word[3] = status;
+            s_word[0] = (uint32_t)(spins < kWaitLimit ? spins : kWaitLimit);   // free since the run list loaded
         }
+        __syncthreads();
+        const uint32_t status = s_word[3];
+        cur.spins = (int64_t)s_word[0];
+        if (status == 2u) {   // uniform
+            // the run's units are [first * tiles, (first + chunks) * tiles)
+            *w_lo = share_of(total, first * (uint32_t)tiles);
+            *w_hi = share_of(total, (first + chunks) * (uint32_t)tiles - 1u) + 1u;   // <= gridDim.x
+            __syncthreads();   // every thread has read s_word before the caller reuses it
+            return true;
+        }
+        const bool task_ok = status == 1u;
+        cur.have_task = false;
         __syncthreads();
         if (task_ok) {   // uniform
             const int wc = (int)(hidden - col0 < wdt ? hidden - col0 : wdt);
@@ -936,21 +949,47 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     // all waves of the workgroup are past their short runs and the flag
     if (!ready && (tid & 63) == 0) atomicOr(&s_word[0], 1u);
     __syncthreads();
+    // shares [w, w_end) to process next, claimed with `mark` (0: already held)
+    uint32_t w = 0u, w_end = 0u, mark = 0u;
+    CombineCursor cur;
+    cur.have_task = false;
+    cur.task = 0u;
+    cur.spins = 0;
+    cur.n_lc = cur.n_lr = 0u;
     if (s_word[0] == 0u) {   // uniform: every wave saw the flag
-        const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
-        const uint32_t n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
         // this workgroup's own share, unless a waiting combine task took it already
-        // (a test setting leaves every other share to the combine tasks)
-        if (!(defer_odd_shares && (blockIdx.x & 1u)))
-            long_units<G, M, VEC>(sm.lng, blockIdx.x, 1u, shares, hdr, units_rs, done, n_lc, n_lr,
-                                  n, grad, grad_stride, partial, partial_stride, hidden, tiles,
-                                  epoch);
+        // (a test setting leaves every other share to the combine tasks); the
+        // claim is in flight together with the loads of the counts
+        if (tid == 0)
+            s_word[1] = !(defer_odd_shares && (blockIdx.x & 1u)) && claim_share(shares, blockIdx.x, 1u);
+        cur.n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
+        cur.n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
+        __syncthreads();
+        if (s_word[1]) {
+            w = blockIdx.x;
+            w_end = w + 1u;
+        }
     }
     const bool flag_seen = s_word[0] == 0u;
     __syncthreads();
-    combine_tasks<G, M, VEC>(sm, s_word, hdr, units_rs, runs_rs, done, shares, flag_seen, n, grad,
-                             grad_stride, partial, partial_stride, main_grad, mg_stride, hidden,
-                             tiles, num_embeddings, n_lc_max, n_lr_max, epoch);
+    // phases 3 and 4: the own share, then combine tasks; a combine task that
+    // waits long hands back the shares its run still needs, taken over here
+    // (one copy of the long-unit code serves both)
+    for (;;) {
+        for (; w < w_end; ++w) {
+            const bool took = long_units<G, M, VEC>(sm.lng, w, mark, shares, hdr, units_rs, done,
+                                                    cur.n_lc, cur.n_lr, n, grad, grad_stride,
+                                                    partial, partial_stride, hidden, tiles, epoch);
+            if (took && mark != 0u && tid == 0)
+                fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);
+            __syncthreads();
+        }
+        if (!combine_tasks<G, M, VEC>(sm, s_word, cur, &w, &w_end, hdr, runs_rs, done, flag_seen,
+                                      partial, partial_stride, main_grad, mg_stride, hidden,
+                                      tiles, num_embeddings, n_lc_max, n_lr_max))
+            break;
+        mark = 2u;
+    }
 
     // ---- phase 5: the last workgroup out resets the call's shared state ----
     // two levels of counters, so that no address takes more than ~32 atomics

@@ -100,7 +100,7 @@ inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     l.runs = round_up(l.units + kUnitRecordBytes * (size_t)(l.max_long_chunks + 1), 256);
     l.done = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
     l.shares = round_up(l.done + 4 * kDoneStride * kDoneGroups * (size_t)(l.max_long_runs + 1), 256);
-    l.partial = round_up(l.shares + 4 * (size_t)kMaxGrid, 256);
+    l.partial = round_up(l.shares + 4 * kDoneStride * (size_t)kMaxGrid, 256);
     l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
     l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
                                        (size_t)l.max_long_chunks, 256);
