@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["accumulate.hip", "sort_lds.h", "ewg_device.h", "ewg_internal.h"]
+KERNEL_SOURCES = ["accumulate.hip", "chunk_sums.h", "sort_lds.h", "ewg_device.h", "ewg_internal.h"]
 
 
 def parse_args():

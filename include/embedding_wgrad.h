@@ -226,6 +226,60 @@ int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,
                                            void *workspace, size_t workspace_bytes,
                                            hipStream_t stream);
 
+/*
+ * Calls of more tokens than the page's MAX_TOKENS. That bound comes from the
+ * page's one-program sort of at most 8192 keys, not from the arithmetic
+ * (introduction; _sort_tokens_kernel sorts one block of keys): this form
+ * gives exactly the result the arithmetic above defines, bit for bit, for
+ * EWG_MIN_TOKENS <= num_tokens <= EWG_MANY_MAX_TOKENS (and the same bits as
+ * accumulate_embedding_wgrad where both apply).
+ *
+ * The batch is cut into tiles of 8192 positions, each sorted in LDS by one
+ * workgroup, and the sorted tiles are merged by rank (a position of tile t
+ * precedes every position of tile t + 1). Five kernels on `stream`; none
+ * waits for another workgroup, so any number of them may run at once.
+ *
+ * can_accumulate_embedding_wgrad_many_tokens: 1 iff
+ *   EWG_MIN_TOKENS <= num_tokens <= EWG_MANY_MAX_TOKENS,
+ *   1 <= num_embeddings <= EWG_MANY_MAX_EMBEDDINGS (a tile key packs the id
+ *   above 13 position bits into 31 bits), hidden >= 1, and the dtypes of
+ *   can_accumulate_embedding_wgrad. Host only.
+ * accumulate_embedding_wgrad_many_tokens_workspace_bytes: bytes of workspace
+ *   for these sizes (0 if out of range). The workspace needs no clearing:
+ *   a call writes every part of it before reading it. Its first int32 is the
+ *   invalid-id count, as for accumulate_embedding_wgrad.
+ * accumulate_embedding_wgrad_many_tokens: arguments, layouts, the id rule
+ *   (an id outside [0, num_embeddings) makes the call change nothing in
+ *   main_grad and stores the number of such ids in the first int32 of the
+ *   workspace), errors and alignment as for accumulate_embedding_wgrad.
+ * ..._timed: with 2 caller-created events recorded on `stream` before the
+ *   first and after the last kernel (benchmarks).
+ */
+#define EWG_MANY_MAX_TOKENS 131072
+#define EWG_MANY_MAX_EMBEDDINGS 262144
+
+int can_accumulate_embedding_wgrad_many_tokens(int64_t num_tokens, int64_t hidden,
+                                               int64_t num_embeddings, int ids_dtype,
+                                               int grad_dtype, int main_grad_dtype);
+
+size_t accumulate_embedding_wgrad_many_tokens_workspace_bytes(int64_t num_tokens, int64_t hidden);
+
+int accumulate_embedding_wgrad_many_tokens(const void *ids, const void *grad, void *main_grad,
+                                           int64_t num_tokens, int64_t hidden,
+                                           int64_t num_embeddings, int64_t grad_row_stride,
+                                           int64_t main_grad_row_stride, int ids_dtype,
+                                           int grad_dtype, int main_grad_dtype, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+int accumulate_embedding_wgrad_many_tokens_timed(const void *ids, const void *grad,
+                                                 void *main_grad, int64_t num_tokens,
+                                                 int64_t hidden, int64_t num_embeddings,
+                                                 int64_t grad_row_stride,
+                                                 int64_t main_grad_row_stride, int ids_dtype,
+                                                 int grad_dtype, int main_grad_dtype,
+                                                 void *workspace, size_t workspace_bytes,
+                                                 hipStream_t stream, hipEvent_t *events);
+
 /* Static English text for a status code (never NULL). */
 const char *ewg_status_string(int status);
 

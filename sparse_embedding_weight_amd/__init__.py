@@ -8,15 +8,21 @@ The work runs in hand-written HIP kernels behind the C ABI of
 include/embedding_wgrad.h; this package is a thin binding to it.
 """
 from ._binding import (  # noqa: F401
+    MANY_MAX_EMBEDDINGS,
+    MANY_MAX_TOKENS,
     MAX_TOKENS,
     MIN_TOKENS,
     NROWS,
     EmbeddingWgradError,
     accumulate_embedding_wgrad,
+    accumulate_embedding_wgrad_many_tokens,
     accumulate_embedding_wgrad_vocab_shard,
     can_accumulate_embedding_wgrad,
+    can_accumulate_embedding_wgrad_many_tokens,
     can_accumulate_embedding_wgrad_vocab_shard,
     invalid_id_count,
+    many_tokens_workspace_bytes,
+    new_many_tokens_workspace,
     new_workspace,
     position_bits,
     sort_tokens,

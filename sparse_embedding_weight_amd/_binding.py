@@ -23,6 +23,8 @@ lib = ctypes.CDLL(LIBRARY)
 MIN_TOKENS = 3073
 MAX_TOKENS = 8192
 NROWS = 10
+MANY_MAX_TOKENS = 131072          # EWG_MANY_MAX_TOKENS
+MANY_MAX_EMBEDDINGS = 262144      # EWG_MANY_MAX_EMBEDDINGS
 
 EWG_INT32, EWG_INT64, EWG_BF16, EWG_FP32 = 0, 1, 2, 3
 EWG_OK, EWG_UNSUPPORTED, EWG_INVALID_ARGUMENT, EWG_WORKSPACE_TOO_SMALL, EWG_HIP_ERROR = range(5)
@@ -40,6 +42,10 @@ EXPORTS = (
     "can_accumulate_embedding_wgrad_vocab_shard",
     "accumulate_embedding_wgrad_vocab_shard",
     "accumulate_embedding_wgrad_sort_tokens",
+    "can_accumulate_embedding_wgrad_many_tokens",
+    "accumulate_embedding_wgrad_many_tokens_workspace_bytes",
+    "accumulate_embedding_wgrad_many_tokens",
+    "accumulate_embedding_wgrad_many_tokens_timed",
     "ewg_status_string",
 )
 
@@ -63,6 +69,14 @@ lib.accumulate_embedding_wgrad_vocab_shard.argtypes = [_vp, _vp, _vp, _i64, _i64
 lib.accumulate_embedding_wgrad_vocab_shard.restype = _int
 lib.accumulate_embedding_wgrad_sort_tokens.argtypes = [_vp, _i64, _i64, _int] + [_vp] * 6 + [_vp, _sz, _vp]
 lib.accumulate_embedding_wgrad_sort_tokens.restype = _int
+lib.can_accumulate_embedding_wgrad_many_tokens.argtypes = [_i64, _i64, _i64, _int, _int, _int]
+lib.can_accumulate_embedding_wgrad_many_tokens.restype = _int
+lib.accumulate_embedding_wgrad_many_tokens_workspace_bytes.argtypes = [_i64, _i64]
+lib.accumulate_embedding_wgrad_many_tokens_workspace_bytes.restype = _sz
+lib.accumulate_embedding_wgrad_many_tokens.argtypes = _ACC_ARGS
+lib.accumulate_embedding_wgrad_many_tokens.restype = _int
+lib.accumulate_embedding_wgrad_many_tokens_timed.argtypes = _ACC_ARGS + [_vp]
+lib.accumulate_embedding_wgrad_many_tokens_timed.restype = _int
 lib.ewg_status_string.argtypes = [_int]
 lib.ewg_status_string.restype = ctypes.c_char_p
 
@@ -228,6 +242,65 @@ def accumulate_embedding_wgrad_vocab_shard(ids: torch.Tensor, grad: torch.Tensor
             ws.data_ptr(), ws.numel(), _stream_handle(main_grad_shard.device))
     if st != EWG_OK:
         raise EmbeddingWgradError(st, "accumulate_embedding_wgrad_vocab_shard")
+
+
+def many_tokens_workspace_bytes(num_tokens: int, hidden: int) -> int:
+    return lib.accumulate_embedding_wgrad_many_tokens_workspace_bytes(num_tokens, hidden)
+
+
+def can_accumulate_embedding_wgrad_many_tokens(ids: torch.Tensor, grad: torch.Tensor,
+                                               main_grad: torch.Tensor) -> bool:
+    """Whether accumulate_embedding_wgrad_many_tokens supports these tensors: as
+    can_accumulate_embedding_wgrad, but MIN_TOKENS..MANY_MAX_TOKENS tokens and at
+    most MANY_MAX_EMBEDDINGS rows of main_grad (no position packing)."""
+    if not _same_layout(ids, grad, main_grad):
+        return False
+    return bool(lib.can_accumulate_embedding_wgrad_many_tokens(
+        ids.numel(), grad.shape[-1], main_grad.shape[0], DTYPE_CODE[ids.dtype],
+        DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad.dtype]))
+
+
+def new_many_tokens_workspace(num_tokens: int, hidden: int, device) -> torch.Tensor:
+    """A workspace for many-token calls with these sizes (needs no clearing)."""
+    return torch.empty(many_tokens_workspace_bytes(num_tokens, hidden), dtype=torch.uint8,
+                       device=device)
+
+
+_MANY_WORKSPACES = {}
+
+
+def accumulate_embedding_wgrad_many_tokens(ids: torch.Tensor, grad: torch.Tensor,
+                                           main_grad: torch.Tensor,
+                                           workspace: torch.Tensor = None) -> None:
+    """accumulate_embedding_wgrad for more than MAX_TOKENS tokens (up to
+    MANY_MAX_TOKENS): the same arithmetic, bit for bit. workspace: optional uint8
+    device tensor of >= many_tokens_workspace_bytes(num_tokens, hidden) bytes
+    (new_many_tokens_workspace() makes one); by default a cached one per device and
+    stream. Requires can_accumulate_embedding_wgrad_many_tokens; raises ValueError
+    otherwise. Enqueued on the current stream of main_grad's device; no sync."""
+    if not can_accumulate_embedding_wgrad_many_tokens(ids, grad, main_grad):
+        raise ValueError("accumulate_embedding_wgrad_many_tokens: unsupported inputs "
+                         "(see can_accumulate_embedding_wgrad_many_tokens)")
+    n, hidden = ids.numel(), grad.shape[-1]
+    ids_flat, grad2 = _flat_inputs(ids, grad)
+    device = main_grad.device
+    need = many_tokens_workspace_bytes(n, hidden)
+    if workspace is None:
+        key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+        workspace = _MANY_WORKSPACES.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+            _MANY_WORKSPACES[key] = workspace
+    if workspace.dtype != torch.uint8 or workspace.device != device or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {device}")
+    with torch.cuda.device(device):
+        st = lib.accumulate_embedding_wgrad_many_tokens(
+            ids_flat.data_ptr(), grad2.data_ptr(), main_grad.data_ptr(), n, hidden,
+            main_grad.shape[0], grad2.stride(0), main_grad.stride(0), DTYPE_CODE[ids.dtype],
+            DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad.dtype], workspace.data_ptr(),
+            workspace.numel(), _stream_handle(device))
+    if st != EWG_OK:
+        raise EmbeddingWgradError(st, "accumulate_embedding_wgrad_many_tokens")
 
 
 def sort_tokens(ids: torch.Tensor, num_embeddings: int, workspace: torch.Tensor = None) -> dict:

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libembedding_wgrad.so")
-SOURCES = ["api.hip", "sort_tokens.hip", "accumulate.hip"]
+SOURCES = ["api.hip", "sort_tokens.hip", "accumulate.hip", "many_tokens.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -152,6 +152,40 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
     return EWG_OK;
 }
 
+// One call of the many-token path.
+int accumulate_many(const void *ids, const void *grad, void *main_grad, int64_t num_tokens,
+                    int64_t hidden, int64_t num_embeddings, int64_t grad_row_stride,
+                    int64_t main_grad_row_stride, int ids_dtype, int grad_dtype,
+                    int main_grad_dtype, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream, hipEvent_t *events) {
+    if (!is_known_dtype(ids_dtype) || !is_known_dtype(grad_dtype) || !is_known_dtype(main_grad_dtype))
+        return EWG_INVALID_ARGUMENT;
+    if (!can_accumulate_embedding_wgrad_many_tokens(num_tokens, hidden, num_embeddings, ids_dtype,
+                                                    grad_dtype, main_grad_dtype))
+        return EWG_UNSUPPORTED;
+    if (!ids || !grad || !main_grad) return EWG_INVALID_ARGUMENT;
+    if (grad_row_stride < hidden || main_grad_row_stride < hidden) return EWG_INVALID_ARGUMENT;
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return EWG_INVALID_ARGUMENT;
+    const ManyLayout l = many_layout(num_tokens, hidden);
+    if (workspace_bytes < l.total) return EWG_WORKSPACE_TOO_SMALL;
+
+    const size_t gs = float_size(grad_dtype), ms = float_size(main_grad_dtype);
+    const int vec_g = (int)(16 / gs);
+    const bool vec = aligned(grad, grad_row_stride * (int64_t)gs, 16) &&
+                     aligned(main_grad, main_grad_row_stride * (int64_t)ms,
+                             vec_g * ms < 16 ? vec_g * ms : 16);
+    (void)hipGetLastError();
+    if (events && hipEventRecord(events[0], stream) != hipSuccess) return EWG_HIP_ERROR;
+    int st = to_status(launch_many_tokens(
+        ids_dtype == EWG_INT64, grad_dtype == EWG_BF16, main_grad_dtype == EWG_BF16, vec, ids,
+        (int)num_tokens, (int)num_embeddings, bit_length((uint64_t)(num_embeddings - 1)), grad,
+        grad_row_stride, main_grad, main_grad_row_stride, (int)hidden, workspace, l, num_cus(),
+        stream));
+    if (st != EWG_OK) return st;
+    if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;
+    return EWG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +280,48 @@ int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,
                                         (int)num_embeddings, ewg_position_bits(num_tokens),
                                         bit_length((uint64_t)(num_embeddings - 1)), workspace, l,
                                         tables, stream));
+}
+
+int can_accumulate_embedding_wgrad_many_tokens(int64_t num_tokens, int64_t hidden,
+                                               int64_t num_embeddings, int ids_dtype,
+                                               int grad_dtype, int main_grad_dtype) {
+    if (num_tokens < EWG_MIN_TOKENS || num_tokens > EWG_MANY_MAX_TOKENS) return 0;
+    if (hidden < 1 || hidden > kMaxHidden) return 0;
+    if (num_embeddings < 1 || num_embeddings > EWG_MANY_MAX_EMBEDDINGS) return 0;
+    if (!is_index_dtype(ids_dtype) || !is_float_dtype(grad_dtype) || !is_float_dtype(main_grad_dtype))
+        return 0;
+    return 1;
+}
+
+size_t accumulate_embedding_wgrad_many_tokens_workspace_bytes(int64_t num_tokens, int64_t hidden) {
+    if (num_tokens < 1 || num_tokens > EWG_MANY_MAX_TOKENS || hidden < 1 || hidden > kMaxHidden)
+        return 0;
+    return many_layout(num_tokens, hidden).total;
+}
+
+int accumulate_embedding_wgrad_many_tokens(const void *ids, const void *grad, void *main_grad,
+                                           int64_t num_tokens, int64_t hidden,
+                                           int64_t num_embeddings, int64_t grad_row_stride,
+                                           int64_t main_grad_row_stride, int ids_dtype,
+                                           int grad_dtype, int main_grad_dtype, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+    return accumulate_many(ids, grad, main_grad, num_tokens, hidden, num_embeddings,
+                           grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                           main_grad_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int accumulate_embedding_wgrad_many_tokens_timed(const void *ids, const void *grad,
+                                                 void *main_grad, int64_t num_tokens,
+                                                 int64_t hidden, int64_t num_embeddings,
+                                                 int64_t grad_row_stride,
+                                                 int64_t main_grad_row_stride, int ids_dtype,
+                                                 int grad_dtype, int main_grad_dtype,
+                                                 void *workspace, size_t workspace_bytes,
+                                                 hipStream_t stream, hipEvent_t *events) {
+    if (!events) return EWG_INVALID_ARGUMENT;
+    return accumulate_many(ids, grad, main_grad, num_tokens, hidden, num_embeddings,
+                           grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                           main_grad_dtype, workspace, workspace_bytes, stream, events);
 }
 
 const char *ewg_status_string(int status) {

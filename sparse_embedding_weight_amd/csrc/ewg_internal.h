@@ -107,6 +107,54 @@ inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
     return l;
 }
 
+// ---- calls of more than kMaxTokens tokens (many_tokens.hip) ------------------
+
+constexpr int kManyMaxTokens = EWG_MANY_MAX_TOKENS;
+static_assert(kManyMaxTokens % 8192 == 0, "whole tiles");
+constexpr int kManyMaxTiles = kManyMaxTokens / kMaxTokens;  // tiles of one LDS sort each
+
+// First bytes of the workspace of a many-token call. The first int32 is the
+// invalid-id count, as in the one-kernel workspace; the rest is written by
+// every call before it is read.
+struct ManyHeader {
+    int32_t invalid_ids;
+    uint32_t n_chunks, n_long_runs, n_long_chunks, n_tasks;
+    int32_t tile_bad[kManyMaxTiles];   // invalid ids per tile
+};
+static_assert(sizeof(ManyHeader) <= 256, "many-token header fits its 256 bytes");
+
+struct ManyLayout {
+    size_t tkeys;            // uint32 per position: each tile's keys, sorted
+    size_t gpos, gid, cw, glen;  // per global rank: position, id, chunk-head word, run length
+    size_t chunks;           // 16-byte record per chunk (first rank, rows, row, partial row)
+    size_t runs;             // 16-byte record per long run (row, first partial row, chunks, first task)
+    size_t partial;          // float[max_long_chunks][partial_stride]
+    size_t total;
+    int64_t partial_stride;
+    int64_t max_long_chunks;
+    int64_t max_long_runs;
+};
+
+inline ManyLayout many_layout(int64_t num_tokens, int64_t hidden) {
+    ManyLayout l;
+    const size_t n = (size_t)num_tokens;
+    const size_t tiles = (n + kMaxTokens - 1) / kMaxTokens;
+    l.max_long_chunks = 2 * num_tokens / 11;
+    l.max_long_runs = num_tokens / 11;
+    l.tkeys = 256;
+    l.gpos = round_up(l.tkeys + 4 * tiles * kMaxTokens, 256);
+    l.gid = round_up(l.gpos + 4 * n, 256);
+    l.cw = round_up(l.gid + 4 * n, 256);
+    l.glen = round_up(l.cw + 4 * n, 256);
+    l.chunks = round_up(l.glen + 4 * n, 256);
+    l.runs = round_up(l.chunks + 16 * n, 256);
+    l.partial = round_up(l.runs + 16 * (size_t)(l.max_long_runs + 1), 256);
+    l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
+    l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
+                                       (size_t)l.max_long_chunks, 256);
+    return l;
+}
+
 // ---- launchers (one per kernel family; defined next to the kernels) --------
 
 // Sort + run marking with the tables written out. One workgroup.
@@ -121,6 +169,16 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
 // num_embeddings; with skip_outside other ids are left out, else they are
 // invalid (the call then touches nothing and reports them). defer_odd_shares
 // (tests only) leaves the long shares of odd workgroups to the combine tasks.
+// Calls of kMaxTokens < n <= kManyMaxTokens tokens (any n >= 1 works): five
+// kernels (tile sort, ranks, chunk lists, chunk sums, ordered combine), same
+// arithmetic as launch_accumulate. Ids must lie in [0, num_embeddings) with
+// num_embeddings <= 2^18; otherwise the call touches nothing and reports them.
+hipError_t launch_many_tokens(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
+                              const void *ids, int n, int num_embeddings, int id_bits,
+                              const void *grad, int64_t grad_stride, void *main_grad,
+                              int64_t mg_stride, int hidden, void *workspace,
+                              const ManyLayout &l, int num_cus, hipStream_t stream);
+
 hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
                              const void *ids, int n, int num_embeddings, int64_t id_base,
                              bool skip_outside, int pos_bits, int id_bits,

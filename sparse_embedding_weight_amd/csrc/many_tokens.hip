@@ -1,0 +1,405 @@
+// Calls of more than 8192 tokens (up to kManyMaxTokens), with the same
+// arithmetic as the one-kernel path: the batch is cut into tiles of 8192
+// positions, each sorted in LDS by one workgroup, and the sorted tiles are
+// merged by rank instead of re-sorted. Five kernels on one stream; each
+// depends only on the ones before it, so no workgroup waits for another.
+//
+// Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
+// introduction (ids sorted with their positions; each id's rows summed in
+// position order into fp32 partial sums of up to 10 rows counted from its
+// first row, the partial sums added in order from 0, one rounding to the
+// gradient dtype, the add into main_grad in fp32), _sort_tokens_kernel,
+// _partial_sums_kernel and _long_run_sums_kernel. The one-program sort of at
+// most 8192 keys is what bounds MAX_TOKENS there; nothing in the arithmetic
+// depends on that bound.
+//
+//   1. tile_sort_kernel (one workgroup per tile): keys (id << 13 | position
+//      in the tile) radix-sorted in LDS (sort_lds.h), written out sorted.
+//   2. rank_kernel (one workgroup per 1024 sorted keys of a tile): every
+//      position of tile t precedes every position of tile t + 1, so the
+//      global (id, position) rank of a key is its index in its own sorted
+//      tile plus, in every earlier tile, the keys with id <= its id and, in
+//      every later tile, the keys with id < its id (binary searches). The
+//      same searches give its run: first rank (keys with a smaller id) and
+//      length (keys with its id). Writes per rank: position, id, and a word
+//      that marks the first row of every chunk (chunks of 10 counted from the
+//      run's first rank) with its row count and whether the run is long.
+//   3. chunk_list_kernel (one workgroup per 8192 ranks): prefix counts of the
+//      marked ranks give every chunk its record (first rank, rows, main_grad
+//      row, partial row for a chunk of a long run) and every long run its
+//      record (row, first partial row, chunk count, first combine task).
+//   4. chunk_sums_kernel: waves take (chunk, group of 4 column tiles) units
+//      in turn; a chunk of a run of at most 10 rows is finished into
+//      main_grad, a chunk of a longer run stored as a partial row.
+//   5. combine_kernel: one (long run, block of columns) task per workgroup
+//      at a time: partial rows added in chunk order from +0, rounded,
+//      added to main_grad (chunk_sums.h combine_block).
+#include "chunk_sums.h"
+#include "ewg_device.h"
+#include "ewg_internal.h"
+#include "sort_lds.h"
+
+namespace ewg {
+namespace {
+
+constexpr int kTileBits = 13;              // positions inside a tile
+constexpr int kTileKeys = 1 << kTileBits;  // keys one workgroup sorts
+static_assert(kTileKeys == kMaxTokens, "a tile is one LDS sort");
+constexpr int kRankSlice = kSortThreads;   // sorted keys per rank_kernel workgroup
+constexpr int kSumThreads = 256;           // chunk_sums_kernel workgroup
+
+// Word per sorted rank: 0, or the first row of a chunk: bit 0 set, rows - 1
+// in bits 1..4, bit 5 if the run has more than 10 rows, bit 6 if the chunk is
+// the run's first.
+constexpr uint32_t kHeadChunk = 1u, kHeadLong = 1u << 5, kHeadRun = 1u << 6;
+
+__device__ __forceinline__ bool any_bad(const ManyHeader *hdr, int tiles, int32_t *sum) {
+    int32_t s = 0;
+    for (int k = 0; k < tiles; ++k) s += hdr->tile_bad[k];
+    *sum = s;
+    return s != 0;
+}
+
+// ---- 1. tile sort ----------------------------------------------------------
+
+template <typename IdT>
+__global__ __launch_bounds__(kSortThreads) void tile_sort_kernel(const IdT *__restrict__ ids, int n,
+                                                                 int num_embeddings, int id_bits,
+                                                                 ManyHeader *__restrict__ hdr,
+                                                                 uint32_t *__restrict__ tkeys) {
+    __shared__ SortSmem sm;
+    const int t = blockIdx.x, base = t * kTileKeys;
+    const int nt = n - base < kTileKeys ? n - base : kTileKeys;
+    const int bad = load_keys<IdT>(sm, ids + base, nt, num_embeddings, kTileBits, 0, false);
+    const int cur = radix_sort_ids(sm, kTileBits, id_bits);
+    for (int i = threadIdx.x; i < nt; i += kSortThreads) tkeys[base + i] = sm.keys[cur][i];
+    if (threadIdx.x == 0) hdr->tile_bad[t] = bad;
+}
+
+// ---- 2. global ranks -------------------------------------------------------
+
+// Number of keys below `key` in each of the tiles, for `key_a` and `key_b`
+// at once: branch-free binary searches in lockstep (one step of every search
+// per round, so all their loads are in flight together).
+__device__ __forceinline__ void count_below(const uint32_t *__restrict__ tkeys, int n, int tiles,
+                                            uint32_t key_a, uint32_t key_b,
+                                            uint32_t (&below_a)[kManyMaxTiles],
+                                            uint32_t (&below_b)[kManyMaxTiles]) {
+#pragma unroll
+    for (int k = 0; k < kManyMaxTiles; ++k) below_a[k] = below_b[k] = 0u;
+#pragma unroll
+    for (int b = kTileBits; b >= 0; --b) {
+        uint32_t va[kManyMaxTiles], vb[kManyMaxTiles];
+#pragma unroll
+        for (int k = 0; k < kManyMaxTiles; ++k) {
+            const int nk = n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys;
+            const uint32_t ca = below_a[k] + (1u << b), cb = below_b[k] + (1u << b);
+            va[k] = k < tiles && ca <= (uint32_t)nk ? tkeys[k * kTileKeys + ca - 1] : 0xffffffffu;
+            vb[k] = k < tiles && cb <= (uint32_t)nk ? tkeys[k * kTileKeys + cb - 1] : 0xffffffffu;
+        }
+#pragma unroll
+        for (int k = 0; k < kManyMaxTiles; ++k) {
+            if (va[k] < key_a) below_a[k] += 1u << b;
+            if (vb[k] < key_b) below_b[k] += 1u << b;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles,
+                                                            const ManyHeader *__restrict__ hdr,
+                                                            const uint32_t *__restrict__ tkeys,
+                                                            int32_t *__restrict__ gpos,
+                                                            uint32_t *__restrict__ gid,
+                                                            uint32_t *__restrict__ cw,
+                                                            uint32_t *__restrict__ glen) {
+    __shared__ uint32_t s_res[3][kRankSlice];   // per id of the slice: before, run start, run length
+    __shared__ uint64_t s_scan[kSortWaves + 1];
+    int32_t bad;
+    if (any_bad(hdr, tiles, &bad)) return;   // uniform: nothing is accumulated
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x / (kTileKeys / kRankSlice);
+    const int i = (blockIdx.x % (kTileKeys / kRankSlice)) * kRankSlice + tid;   // index in the sorted tile
+    const int nt = n - t * kTileKeys < kTileKeys ? n - t * kTileKeys : kTileKeys;
+    const bool valid = i < nt;
+    const uint32_t key = valid ? tkeys[t * kTileKeys + i] : 0xffffffffu;
+    const uint32_t x = key >> kTileBits;
+    const bool head = valid && (tid == 0 || (tkeys[t * kTileKeys + i - 1] >> kTileBits) != x);
+    uint64_t heads;
+    const uint32_t excl = (uint32_t)block_exclusive_scan(head ? 1u : 0u, s_scan, &heads);
+    const uint32_t ord = head ? excl : excl - 1u;   // the slice's id groups in order
+    if (head) {
+        uint32_t lo[kManyMaxTiles], hi[kManyMaxTiles];
+        count_below(tkeys, n, tiles, x << kTileBits, (x + 1u) << kTileBits, lo, hi);
+        uint32_t before = 0u, start = 0u, len = 0u;
+#pragma unroll
+        for (int k = 0; k < kManyMaxTiles; ++k) {
+            start += lo[k];
+            len += hi[k] - lo[k];
+            if (k < t) before += hi[k];       // earlier positions of this id and smaller ids
+            else if (k > t) before += lo[k];  // smaller ids only
+        }
+        s_res[0][ord] = before;
+        s_res[1][ord] = start;
+        s_res[2][ord] = len;
+    }
+    __syncthreads();
+    if (!valid) return;
+    const uint32_t rank = s_res[0][ord] + (uint32_t)i;
+    const uint32_t start = s_res[1][ord], len = s_res[2][ord];
+    if (rank >= (uint32_t)n) return;   // never: the ranks of the n keys are 0 .. n-1
+    const uint32_t off = rank - start;
+    gpos[rank] = t * kTileKeys + (int32_t)(key & (kTileKeys - 1));
+    gid[rank] = x;
+    uint32_t w = 0u;
+    if (off % kNRows == 0) {
+        const uint32_t rows = len - off < (uint32_t)kNRows ? len - off : (uint32_t)kNRows;
+        w = kHeadChunk | ((rows - 1u) << 1) | (len > (uint32_t)kNRows ? kHeadLong : 0u) |
+            (off == 0 ? kHeadRun : 0u);
+    }
+    cw[rank] = w;
+    if (off == 0) glen[rank] = len;
+}
+
+// ---- 3. chunk and long-run lists -------------------------------------------
+
+// Combine tasks of a long run of `len` rows: blocks of combine_width columns.
+__device__ __forceinline__ uint32_t run_tasks(uint32_t len, int hidden) {
+    const int chunks = (int)((len + kNRows - 1) / kNRows);
+    const int w = combine_width(chunks, hidden);
+    return (uint32_t)((hidden + w - 1) / w);
+}
+
+// counters packed in 21-bit fields: chunks, long runs, long chunks
+__device__ __forceinline__ uint64_t head_counts(uint32_t w) {
+    if (!(w & kHeadChunk)) return 0;
+    const bool lng = (w & kHeadLong) != 0;
+    return 1ull | ((uint64_t)(lng && (w & kHeadRun)) << 21) | ((uint64_t)lng << 42);
+}
+
+constexpr uint64_t kField = (1ull << 21) - 1;
+
+__global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int tiles, int hidden,
+                                                                  uint32_t max_long_runs,
+                                                                  uint32_t max_long_chunks,
+                                                                  ManyHeader *__restrict__ hdr,
+                                                                  const uint32_t *__restrict__ gid,
+                                                                  const uint32_t *__restrict__ cw,
+                                                                  const uint32_t *__restrict__ glen,
+                                                                  u32x4 *__restrict__ chunks,
+                                                                  u32x4 *__restrict__ runs) {
+    __shared__ uint64_t s_scan[kSortWaves + 1];
+    const int tid = threadIdx.x;
+    int32_t bad;
+    if (any_bad(hdr, tiles, &bad)) {   // uniform
+        if (blockIdx.x == 0 && tid == 0) {
+            hdr->invalid_ids = bad;
+            hdr->n_chunks = hdr->n_long_runs = hdr->n_long_chunks = hdr->n_tasks = 0u;
+        }
+        return;
+    }
+    const int r0 = blockIdx.x * kTileKeys;
+    // counts over the ranks of earlier blocks (each block recounts them: no
+    // block waits for another)
+    uint64_t pre = 0, pre_tasks = 0;
+    for (int r = tid * 4; r < r0; r += kSortThreads * 4) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(cw + r);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pre += head_counts(w4[j]);
+            if ((w4[j] & (kHeadChunk | kHeadLong | kHeadRun)) == (kHeadChunk | kHeadLong | kHeadRun))
+                pre_tasks += run_tasks(glen[r + j], hidden);
+        }
+    }
+    uint64_t base, base_tasks;
+    block_exclusive_scan(pre, s_scan, &base);
+    block_exclusive_scan(pre_tasks, s_scan, &base_tasks);
+
+    // this block's ranks: thread j owns [r0 + 8j, r0 + 8j + 8)
+    const int s0 = r0 + tid * kSortItems;
+    uint32_t w[kSortItems];
+    uint64_t mine = 0, mine_tasks = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        w[j] = s0 + j < n ? cw[s0 + j] : 0u;
+        mine += head_counts(w[j]);
+        if ((w[j] & (kHeadChunk | kHeadLong | kHeadRun)) == (kHeadChunk | kHeadLong | kHeadRun))
+            mine_tasks += run_tasks(glen[s0 + j], hidden);
+    }
+    uint64_t all, all_tasks;
+    uint64_t idx = base + block_exclusive_scan(mine, s_scan, &all);
+    uint64_t task = base_tasks + block_exclusive_scan(mine_tasks, s_scan, &all_tasks);
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        if (w[j] & kHeadChunk) {
+            const uint32_t s = (uint32_t)(s0 + j);
+            const uint32_t c = (uint32_t)(idx & kField);
+            const uint32_t lr = (uint32_t)((idx >> 21) & kField);
+            const uint32_t lc = (uint32_t)((idx >> 42) & kField);
+            const bool lng = (w[j] & kHeadLong) != 0;
+            const uint32_t rows = ((w[j] >> 1) & 15u) + 1u;
+            const uint32_t row = gid[s];
+            // (the bounds hold by construction: at most n chunks, n / 11 long
+            // runs, 2n / 11 long-run chunks)
+            if (c < (uint32_t)n && (!lng || lc < max_long_chunks))
+                chunks[c] = u32x4{s, rows, row, lng ? lc : 0xffffffffu};
+            if (lng && (w[j] & kHeadRun) && lr < max_long_runs) {
+                const uint32_t len = glen[s];
+                runs[lr] = u32x4{row, lc, (len + kNRows - 1) / kNRows, (uint32_t)task};
+                task += run_tasks(len, hidden);
+            }
+            idx += head_counts(w[j]);
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1 && tid == 0) {
+        const uint64_t tot = base + all;
+        hdr->invalid_ids = 0;
+        hdr->n_chunks = (uint32_t)(tot & kField);
+        hdr->n_long_runs = (uint32_t)((tot >> 21) & kField);
+        hdr->n_long_chunks = (uint32_t)((tot >> 42) & kField);
+        hdr->n_tasks = (uint32_t)(base_tasks + all_tasks);
+    }
+}
+
+// ---- 4. chunk sums ---------------------------------------------------------
+
+template <typename G, typename M, int VEC>
+__global__ __launch_bounds__(kSumThreads) void chunk_sums_kernel(
+    int n, int num_embeddings, const ManyHeader *__restrict__ hdr,
+    const u32x4 *__restrict__ chunks, const int32_t *__restrict__ gpos,
+    const typename G::T *__restrict__ grad, int64_t grad_stride,
+    typename M::T *__restrict__ main_grad, int64_t mg_stride, float *__restrict__ partial,
+    int64_t partial_stride, uint32_t max_long_chunks, int hidden, int tiles) {
+    const uint32_t n_chunks = min(hdr->n_chunks, (uint32_t)n);
+    const uint32_t groups = (uint32_t)((tiles + kTilesPerUnit - 1) / kTilesPerUnit);
+    const uint32_t units = n_chunks * groups;
+    const int full_tiles = hidden / (64 * VEC);
+    const uint32_t waves = gridDim.x * (kSumThreads / 64);
+    for (uint32_t u = blockIdx.x * (kSumThreads / 64) + (threadIdx.x >> 6); u < units; u += waves) {
+        const uint32_t c = u / groups, g = u - c * groups;
+        const u32x4 rec = chunks[c];
+        const uint32_t s = __builtin_amdgcn_readfirstlane(rec.x);
+        const uint32_t row = __builtin_amdgcn_readfirstlane(rec.z);
+        const uint32_t dest = __builtin_amdgcn_readfirstlane(rec.w);
+        int rows = (int)__builtin_amdgcn_readfirstlane(rec.y);
+        rows = rows < 1 ? 1 : (rows > kNRows ? kNRows : rows);
+        // a record outside this call's ranges (never expected) is skipped
+        if (row >= (uint32_t)num_embeddings || s + (uint32_t)rows > (uint32_t)n ||
+            (dest != 0xffffffffu && dest >= max_long_chunks))
+            continue;
+        int32_t pos[kNRows];
+#pragma unroll
+        for (int r = 0; r < kNRows; ++r) {
+            const int32_t p = r < rows ? gpos[s + r] : 0;
+            pos[r] = p >= 0 && p < n ? p : 0;   // every row inside grad
+        }
+        const int t0 = (int)g * kTilesPerUnit;
+        const int t_end = t0 + kTilesPerUnit < tiles ? t0 + kTilesPerUnit : tiles;
+        chunk_tiles_any<G, M, VEC>(pos, rows, (int)row, dest == 0xffffffffu ? -1 : (int)dest,
+                                   grad, grad_stride, main_grad, mg_stride, partial,
+                                   partial_stride, hidden, t0, t_end, full_tiles);
+    }
+}
+
+// ---- 5. ordered combine ----------------------------------------------------
+
+template <typename G, typename M>
+__global__ __launch_bounds__(kSortThreads) void combine_kernel(
+    int num_embeddings, const ManyHeader *__restrict__ hdr, const u32x4 *__restrict__ runs,
+    const float *__restrict__ partial, int64_t partial_stride, typename M::T *__restrict__ main_grad,
+    int64_t mg_stride, uint32_t max_long_chunks, uint32_t max_long_runs, int hidden) {
+    __shared__ float stage[kStageFloats];
+    const uint32_t n_tasks = hdr->n_tasks;
+    const int n_lr = (int)min(hdr->n_long_runs, max_long_runs);
+    for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+        // the run: the last one whose first task is at or before t
+        int lo = 0, hi = n_lr;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (runs[mid].w <= t) lo = mid; else hi = mid;
+        }
+        const u32x4 rec = runs[lo];
+        const uint32_t row = rec.x, first = rec.y, chunks = rec.z;
+        const int wdt = combine_width((int)chunks, hidden);
+        const int64_t col0 = (int64_t)(t - rec.w) * wdt;
+        // a record that does not describe this call's work (never expected) is skipped
+        if (n_lr < 1 || rec.w > t || row >= (uint32_t)num_embeddings || chunks < 1 ||
+            first >= max_long_chunks || chunks > max_long_chunks - first || col0 >= hidden)
+            continue;
+        combine_block<G, M>(stage, row, first, chunks, col0, wdt, partial, partial_stride,
+                            main_grad, mg_stride, hidden);
+        __syncthreads();
+    }
+}
+
+// ---- launch ----------------------------------------------------------------
+
+template <typename IdT, typename G, typename M, int VEC>
+hipError_t launch(const void *ids, int n, int num_embeddings, int id_bits, const void *grad,
+                  int64_t grad_stride, void *main_grad, int64_t mg_stride, int hidden,
+                  void *workspace, const ManyLayout &l, int num_cus, hipStream_t stream) {
+    char *ws = static_cast<char *>(workspace);
+    ManyHeader *hdr = reinterpret_cast<ManyHeader *>(ws);
+    uint32_t *tkeys = reinterpret_cast<uint32_t *>(ws + l.tkeys);
+    int32_t *gpos = reinterpret_cast<int32_t *>(ws + l.gpos);
+    uint32_t *gid = reinterpret_cast<uint32_t *>(ws + l.gid);
+    uint32_t *cw = reinterpret_cast<uint32_t *>(ws + l.cw);
+    uint32_t *glen = reinterpret_cast<uint32_t *>(ws + l.glen);
+    u32x4 *chunks = reinterpret_cast<u32x4 *>(ws + l.chunks);
+    u32x4 *runs = reinterpret_cast<u32x4 *>(ws + l.runs);
+    float *partial = reinterpret_cast<float *>(ws + l.partial);
+    const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    const int col_tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
+
+    tile_sort_kernel<IdT><<<tiles, kSortThreads, 0, stream>>>(
+        static_cast<const IdT *>(ids), n, num_embeddings, id_bits, hdr, tkeys);
+    rank_kernel<<<tiles * (kTileKeys / kRankSlice), kSortThreads, 0, stream>>>(
+        n, tiles, hdr, tkeys, gpos, gid, cw, glen);
+    chunk_list_kernel<<<tiles, kSortThreads, 0, stream>>>(
+        n, tiles, hidden, (uint32_t)l.max_long_runs, (uint32_t)l.max_long_chunks, hdr, gid, cw, glen,
+        chunks, runs);
+    chunk_sums_kernel<G, M, VEC><<<num_cus * 8, kSumThreads, 0, stream>>>(
+        n, num_embeddings, hdr, chunks, gpos, static_cast<const typename G::T *>(grad),
+        grad_stride, static_cast<typename M::T *>(main_grad), mg_stride, partial, l.partial_stride,
+        (uint32_t)l.max_long_chunks, hidden, col_tiles);
+    combine_kernel<G, M><<<num_cus, kSortThreads, 0, stream>>>(
+        num_embeddings, hdr, runs, partial, l.partial_stride,
+        static_cast<typename M::T *>(main_grad), mg_stride, (uint32_t)l.max_long_chunks,
+        (uint32_t)l.max_long_runs, hidden);
+    return hipGetLastError();
+}
+
+template <typename IdT>
+hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *ids, int n,
+                          int num_embeddings, int id_bits, const void *grad, int64_t grad_stride,
+                          void *main_grad, int64_t mg_stride, int hidden, void *workspace,
+                          const ManyLayout &l, int num_cus, hipStream_t stream) {
+#define EWG_MANY(G, M, V)                                                                       \
+    launch<IdT, G, M, V>(ids, n, num_embeddings, id_bits, grad, grad_stride, main_grad, mg_stride, \
+                         hidden, workspace, l, num_cus, stream)
+    if (grad_bf16) {
+        if (mg_bf16) return vec ? EWG_MANY(BF16, BF16, 8) : EWG_MANY(BF16, BF16, 1);
+        return vec ? EWG_MANY(BF16, F32, 8) : EWG_MANY(BF16, F32, 1);
+    }
+    if (mg_bf16) return vec ? EWG_MANY(F32, BF16, 4) : EWG_MANY(F32, BF16, 1);
+    return vec ? EWG_MANY(F32, F32, 4) : EWG_MANY(F32, F32, 1);
+#undef EWG_MANY
+}
+
+}  // namespace
+
+hipError_t launch_many_tokens(bool ids_int64, bool grad_bf16, bool mg_bf16, bool vec,
+                              const void *ids, int n, int num_embeddings, int id_bits,
+                              const void *grad, int64_t grad_stride, void *main_grad,
+                              int64_t mg_stride, int hidden, void *workspace,
+                              const ManyLayout &l, int num_cus, hipStream_t stream) {
+    if (ids_int64)
+        return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_bits,
+                                       grad, grad_stride, main_grad, mg_stride, hidden, workspace,
+                                       l, num_cus, stream);
+    return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_bits, grad,
+                                   grad_stride, main_grad, mg_stride, hidden, workspace, l,
+                                   num_cus, stream);
+}
+
+}  // namespace ewg

@@ -162,3 +162,57 @@ def test_vocab_shard_python_predicate():
     assert not ewg.can_accumulate_embedding_wgrad_vocab_shard(ids, grad, mg, 0)   # CPU tensors
     with pytest.raises(ValueError):
         ewg.accumulate_embedding_wgrad_vocab_shard(ids, grad, mg, 0)
+
+
+def test_many_tokens_envelope_and_argument_errors():
+    can_m = B.lib.can_accumulate_embedding_wgrad_many_tokens
+    assert B.MANY_MAX_TOKENS == 131072 and B.MANY_MAX_EMBEDDINGS == 1 << 18
+    assert can_m(8193, 7168, 129280, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert can_m(B.MANY_MAX_TOKENS, 7168, 129280, B.EWG_INT64, B.EWG_FP32, B.EWG_BF16)
+    # the one-kernel range is accepted too (same arithmetic)
+    assert can_m(B.MIN_TOKENS, 1, 1, B.EWG_INT32, B.EWG_FP32, B.EWG_FP32)
+    # no position packing: the table bound is the tile key's, 2^18 rows at any count
+    assert can_m(B.MANY_MAX_TOKENS, 64, 1 << 18, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(16384, 64, (1 << 18) + 1, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(B.MANY_MAX_TOKENS + 1, 64, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(B.MIN_TOKENS - 1, 64, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(20000, 0, 100, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(20000, 64, 0, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32)
+    assert not can_m(20000, 64, 100, B.EWG_BF16, B.EWG_BF16, B.EWG_FP32)
+
+    wsb = ewg.many_tokens_workspace_bytes
+    assert wsb(0, 64) == 0 and wsb(B.MANY_MAX_TOKENS + 1, 64) == 0 and wsb(20000, 0) == 0
+    # the partial rows of the long runs dominate: 2n/11 rows of hidden rounded to 64
+    assert wsb(131072, 7168) >= (2 * 131072 // 11) * 7168 * 4
+    assert wsb(20000, 100) < wsb(20000, 200) and wsb(20000, 100) < wsb(40000, 100)
+
+    def many(**kw):
+        a = dict(ids=8, grad=16, main_grad=32, n=20000, h=64, v=100, gs=64, ms=64,
+                 i=B.EWG_INT32, g=B.EWG_BF16, m=B.EWG_FP32, ws=256 * 1024, wsb=1 << 40)
+        a.update(kw)
+        return B.lib.accumulate_embedding_wgrad_many_tokens(
+            a["ids"], a["grad"], a["main_grad"], a["n"], a["h"], a["v"], a["gs"], a["ms"],
+            a["i"], a["g"], a["m"], a["ws"], a["wsb"], None)
+
+    # every case fails a host check, so nothing touches a device
+    assert many(n=B.MANY_MAX_TOKENS + 1) == B.EWG_UNSUPPORTED
+    assert many(v=(1 << 18) + 1) == B.EWG_UNSUPPORTED
+    assert many(i=9) == B.EWG_INVALID_ARGUMENT
+    assert many(main_grad=None) == B.EWG_INVALID_ARGUMENT
+    assert many(ms=10) == B.EWG_INVALID_ARGUMENT
+    assert many(ws=None) == B.EWG_INVALID_ARGUMENT
+    assert many(ws=256 * 1024 + 8) == B.EWG_INVALID_ARGUMENT
+    assert many(wsb=wsb(20000, 64) - 1) == B.EWG_WORKSPACE_TOO_SMALL
+    assert B.lib.accumulate_embedding_wgrad_many_tokens_timed(
+        8, 16, 32, 20000, 64, 100, 64, 64, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32, 256 * 1024,
+        1 << 40, None, None) == B.EWG_INVALID_ARGUMENT
+
+
+def test_many_tokens_python_predicate():
+    ids = torch.zeros(20000, dtype=torch.int32)
+    grad = torch.zeros(20000, 64)
+    mg = torch.zeros(100, 64)
+    # CPU tensors are never accepted
+    assert not ewg.can_accumulate_embedding_wgrad_many_tokens(ids, grad, mg)
+    with pytest.raises(ValueError):
+        ewg.accumulate_embedding_wgrad_many_tokens(ids, grad, mg)

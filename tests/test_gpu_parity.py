@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads as wl
+from parity_util import _bits, assert_rows_match, oracle_rows  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -21,31 +22,6 @@ ewg = pytest.importorskip("sparse_embedding_weight_amd")
 @pytest.fixture(autouse=True)
 def _gpu(require_gpu):
     yield
-
-
-def _bits(t: torch.Tensor) -> torch.Tensor:
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
-
-
-def _is_nan_bits(a: np.ndarray, dtype: str) -> np.ndarray:
-    if dtype == "bf16":
-        return (a & 0x7FFF) > 0x7F80
-    b = a.view(np.uint32)
-    return (b & 0x7FFFFFFF) > 0x7F800000
-
-
-def oracle_rows(ids: torch.Tensor, grad: torch.Tensor, rows: torch.Tensor,
-                before_rows: torch.Tensor) -> np.ndarray:
-    """Oracle result for the touched rows: ids relabelled to their index in the
-    sorted list of touched rows (an order-preserving relabel)."""
-    g_dt = "bf16" if grad.dtype == torch.bfloat16 else "fp32"
-    m_dt = "bf16" if before_rows.dtype == torch.bfloat16 else "fp32"
-    ids_np = ids.reshape(-1).cpu().numpy()
-    compact = np.searchsorted(rows.cpu().numpy(), ids_np).astype(ids_np.dtype)
-    grad_np = wl.to_numpy_bits(grad.reshape(ids_np.size, grad.shape[-1]).cpu())
-    mg_np = wl.to_numpy_bits(before_rows.cpu()).copy()
-    oracle.accumulate_embedding_wgrad(compact, grad_np, mg_np, g_dt, m_dt)
-    return mg_np
 
 
 _SHARED_WS = {}
@@ -64,7 +40,6 @@ def shared_workspace(n: int, hidden: int) -> torch.Tensor:
 
 def check_call(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor, **kw):
     """Run one call on the GPU and compare with the oracle; returns the touched rows."""
-    m_dt = "bf16" if main_grad.dtype == torch.bfloat16 else "fp32"
     rows = torch.unique(ids.reshape(-1).long())
     before_rows = main_grad[rows].clone()
     before = main_grad.clone()
@@ -75,30 +50,7 @@ def check_call(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor, *
     torch.cuda.synchronize()
     assert ewg.wait_timeouts(ws) == 0, "a bounded wait inside the kernel gave up"
 
-    got = wl.to_numpy_bits(main_grad[rows].cpu())
-    want = oracle_rows(ids, grad, rows, before_rows)
-    nan_g, nan_w = _is_nan_bits(got, m_dt), _is_nan_bits(want, m_dt)
-    assert np.array_equal(nan_g, nan_w), "NaN positions differ"
-    gv = got.view(np.uint16 if m_dt == "bf16" else np.uint32)
-    wv = want.view(np.uint16 if m_dt == "bf16" else np.uint32)
-    mism = (gv != wv) & ~nan_g
-    if mism.any():
-        r, c = np.argwhere(mism)[0]
-        bad_rows = np.flatnonzero(mism.any(axis=1))
-        counts = np.bincount(ids.reshape(-1).long().cpu().numpy())
-        detail = "; ".join(
-            f"id {int(rows[b])} ({int(counts[int(rows[b])])} rows): {int(mism[b].sum())} cols "
-            f"in [{int(np.flatnonzero(mism[b])[0])}, {int(np.flatnonzero(mism[b])[-1])}]"
-            for b in bad_rows[:12])
-        raise AssertionError(f"{int(mism.sum())} mismatching elements in {bad_rows.size} rows; first "
-                             f"at touched row {r} (id {int(rows[r])}), column {c}: got {gv[r, c]:#x} "
-                             f"want {wv[r, c]:#x}; {detail}")
-
-    # untouched rows: bit-identical to the copy taken before the call
-    changed = (_bits(main_grad) != _bits(before)).any(dim=1)
-    touched = torch.zeros(main_grad.shape[0], dtype=torch.bool, device=main_grad.device)
-    touched[rows] = True
-    assert not (changed & ~touched).any(), "a row whose id does not occur was written"
+    assert_rows_match(ids, grad, main_grad, before, rows, before_rows)
     return rows
 
 
@@ -326,19 +278,8 @@ def _shard_calls(ids, grad, mg, bounds, ws=None):
 
 
 def _check_against_oracle(ids, grad, before, after):
-    m_dt = "bf16" if after.dtype == torch.bfloat16 else "fp32"
     rows = torch.unique(ids.reshape(-1).long())
-    got = wl.to_numpy_bits(after[rows].cpu())
-    want = oracle_rows(ids, grad, rows, before[rows].clone())
-    nan_g, nan_w = _is_nan_bits(got, m_dt), _is_nan_bits(want, m_dt)
-    assert np.array_equal(nan_g, nan_w)
-    gv = got.view(np.uint16 if m_dt == "bf16" else np.uint32)
-    wv = want.view(np.uint16 if m_dt == "bf16" else np.uint32)
-    assert int(((gv != wv) & ~nan_g).sum()) == 0
-    changed = (_bits(after) != _bits(before)).any(dim=1)
-    touched = torch.zeros(after.shape[0], dtype=torch.bool, device=after.device)
-    touched[rows] = True
-    assert not (changed & ~touched).any(), "a row whose id does not occur was written"
+    assert_rows_match(ids, grad, after, before, rows, before[rows].clone())
 
 
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))

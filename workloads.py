@@ -20,6 +20,17 @@ Five workloads, named for what they are:
                              ids [4,2048] Zipf(s=1.3) over 129280; grad [4,2048,7168]
                              bf16 ~ N(0, 0.01); main_grad bf16 ~ N(0, 1e-3)
 
+Four more with more tokens than one LDS sort holds (MANY_WORKLOADS, for the
+many-token entry point):
+
+  zipf1.1_32768_v129280_h7168    ids [4,8192] Zipf(s=1.1) over 129280, as the
+                                 headline otherwise
+  zipf1.1_131072_v129280_h7168   ids [16,8192], the largest token count
+  longrun_16384_v129280_h7168    the long-run law at 16384 positions (id 7 on
+                                 8192 of them), fp32 grad
+  zipf1.3_24576_v32000_h4096_bf16mg
+                                 24576 ids Zipf(s=1.3) over 32000, bf16 main_grad
+
 Recipe: numpy's PCG64 (`default_rng(seed)`) draws ids and grad; sigma is the
 standard deviation; bf16 grad is torch's round-to-nearest-even of the fp32
 draw. Zipf(s) over V means P(id = k) proportional to (k + 1)^-s for k in
@@ -71,6 +82,25 @@ WORKLOADS = {
 
 # the headline workload: 8192 tokens into a 129280 x 7168 main_grad
 HEADLINE = "zipf1.1_8192_v129280_h7168"
+
+# more tokens than one LDS sort holds (the many-token entry point): the
+# headline's table and id law with 4x and 16x the tokens (micro-batches of
+# 4 and 16 sequences of 8192), a long-run stress with one id on half of
+# 16384 positions, and a bf16 main_grad with a steeper Zipf law
+MANY_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("zipf1.1_32768_v129280_h7168", (4, 8192), 129280, 7168, "zipf", 1.1,
+                 "bf16", 0.01, "fp32", 1e-3, 6),
+        Workload("zipf1.1_131072_v129280_h7168", (16, 8192), 129280, 7168, "zipf", 1.1,
+                 "bf16", 0.01, "fp32", 1e-3, 7),
+        Workload("longrun_16384_v129280_h7168", (16384,), 129280, 7168, "longrun", 0.0,
+                 "fp32", 1.0, "fp32", 1e-3, 8),
+        Workload("zipf1.3_24576_v32000_h4096_bf16mg", (24576,), 32000, 4096, "zipf", 1.3,
+                 "bf16", 0.01, "bf16", 1e-3, 9),
+    ]
+}
+MANY_HEADLINE = "zipf1.1_32768_v129280_h7168"
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
