@@ -13,7 +13,10 @@ launch stream right before and after the kernel.
 
 Prints one JSON line: value = algorithmic bytes / mean call time (GB/s), the
 roofline of the kernel (the whole call is one kernel), and the CPU oracle
-timed on the host as cpu_baseline.
+timed on the host as cpu_baseline. Also timed, each in its own object: the
+dense PyTorch path on the same inputs (dense_baseline), the many-token entry
+point on a batch of more than 8192 tokens (many_tokens, with its own dense
+baseline), and with --vocab-shards S the vocabulary-shard entry point.
 """
 import argparse
 import ctypes
@@ -52,6 +55,11 @@ def parse_args():
                         "many equal row ranges, one call per shard (reported under vocab_shards)")
     p.add_argument("--no-dense-baseline", action="store_true",
                    help="skip timing PyTorch's dense embedding backward + main_grad.add_")
+    p.add_argument("--many-workload", default=None,
+                   help="workload of the many-token entry point timed under many_tokens "
+                        "(default: the 32768-token one)")
+    p.add_argument("--no-many-tokens", action="store_true",
+                   help="skip timing the many-token entry point")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference for counter scaling)")
     return p.parse_args()
@@ -193,6 +201,55 @@ def dense_baseline(torch, w, ids, grad, mg, flush, flush_sink, flush_mode, our_m
             "speedup_of_fused_call": round(ms / our_ms, 2)}
 
 
+def time_many_tokens(torch, ewg, B, wl, name, hip, flush, flush_sink, flush_mode, steps, warmup,
+                     dense):
+    """The many-token entry point (more tokens than one LDS sort holds) on its own
+    workload: mean µs per call between two HIP events the library records on its
+    stream around its five kernels, caches emptied before each call; GB/s of the
+    same algorithmic bytes as the headline."""
+    w = wl.MANY_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    ids_np = wl.make_ids(w).reshape(-1)
+    ids = torch.from_numpy(ids_np).to(dev)
+    grad = wl.make_grad(w).reshape(w.num_tokens, w.hidden).to(dev)
+    mg = wl.make_main_grad(w, dev)
+    counts = np.bincount(ids_np, minlength=w.vocab)
+    uniq = int((counts > 0).sum())
+    alg = wl.algorithmic_bytes(w.num_tokens, w.hidden, uniq, w.grad_dtype, w.main_grad_dtype,
+                               ids_np.itemsize)
+    ws = ewg.new_many_tokens_workspace(w.num_tokens, w.hidden, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    call_args = (ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), w.num_tokens, w.hidden, w.vocab,
+                 grad.stride(0), mg.stride(0), B.DTYPE_CODE[ids.dtype], B.DTYPE_CODE[grad.dtype],
+                 B.DTYPE_CODE[mg.dtype], ws.data_ptr(), ws.numel(), stream)
+    events = [hip.create(2) for _ in range(warmup + steps)]
+    for k in range(warmup + steps):
+        if flush_mode == "read":
+            flush_sink.copy_(flush.sum())
+        elif flush_mode == "write":
+            flush.fill_(float(k))
+        st = B.lib.accumulate_embedding_wgrad_many_tokens_timed(*call_args, events[k])
+        if st != 0:
+            raise B.EmbeddingWgradError(st, "accumulate_embedding_wgrad_many_tokens_timed")
+    torch.cuda.synchronize()
+    t = np.array([hip.ms(e[0], e[1]) for e in events[warmup:]])
+    for e in events:
+        hip.destroy(e)
+    ms = float(t.mean())
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {"workload": name, "num_tokens": w.num_tokens, "vocab": w.vocab, "hidden": w.hidden,
+           "grad_dtype": w.grad_dtype, "main_grad_dtype": w.main_grad_dtype,
+           "distinct_ids": uniq, "runs_longer_than_10": int((counts > ewg.NROWS).sum()),
+           "algorithmic_bytes": alg, "us_per_call": round(ms * 1e3, 2),
+           "us_per_call_p10_p50_p90": [round(float(np.percentile(t, q)) * 1e3, 2) for q in (10, 50, 90)],
+           "GB_per_s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "kernels": "tile sort, ranks, chunk lists, chunk sums, ordered combine (one stream)"}
+    if dense:
+        out["dense_baseline"] = dense_baseline(torch, w, ids, grad, mg, flush, flush_sink,
+                                               flush_mode, ms)
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -302,6 +359,11 @@ def main():
     if not args.no_dense_baseline:
         result["dense_baseline"] = dense_baseline(torch, w, ids, grad, mg, flush, flush_sink,
                                                   args.flush, mean_call_ms)
+
+    if not args.no_many_tokens:
+        result["many_tokens"] = time_many_tokens(
+            torch, ewg, B, wl, args.many_workload or wl.MANY_HEADLINE, hip, flush, flush_sink,
+            args.flush, args.steps, args.warmup, not args.no_dense_baseline)
 
     if not args.no_cpu_baseline:
         t_cpu, reps = cpu_baseline(w, ids_np, wl.to_numpy_bits(grad_cpu), args.cpu_seconds)

@@ -2,9 +2,11 @@
 
     python sparse_embedding_weight_amd/build.py
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -24,12 +26,25 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (each holds its own kernels
+    and their launchers), then link the shared library."""
     tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory() as objdir:
+        cmds = [[HIPCC, *compile_flags, "-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                 os.path.join(CSRC, s), "-o", os.path.join(objdir, s + ".o")] for s in SOURCES]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), file=sys.stderr)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+            for r in pool.map(lambda c: subprocess.run(c), cmds):
+                if r.returncode != 0:
+                    raise subprocess.CalledProcessError(r.returncode, r.args)
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                *[os.path.join(objdir, s + ".o") for s in SOURCES], "-o", tmp]
+        if verbose:
+            print(" ".join(link), file=sys.stderr)
+        subprocess.run(link, check=True)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

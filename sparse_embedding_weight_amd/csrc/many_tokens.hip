@@ -28,9 +28,10 @@
 //      marked ranks give every chunk its record (first rank, rows, main_grad
 //      row, partial row for a chunk of a long run) and every long run its
 //      record (row, first partial row, chunk count, first combine task).
-//   4. chunk_sums_kernel: waves take (chunk, group of 4 column tiles) units
-//      in turn; a chunk of a run of at most 10 rows is finished into
-//      main_grad, a chunk of a longer run stored as a partial row.
+//   4. chunk_sums_kernel: (chunk, 4 column tiles) units dealt round-robin to
+//      the waves of a grid several times larger than fits at once; a chunk
+//      of a run of at most 10 rows is finished into main_grad, a chunk of a
+//      longer run stored as a partial row.
 //   5. combine_kernel: one (long run, block of columns) task per workgroup
 //      at a time: partial rows added in chunk order from +0, rounded,
 //      added to main_grad (chunk_sums.h combine_block).
@@ -47,11 +48,16 @@ constexpr int kTileKeys = 1 << kTileBits;  // keys one workgroup sorts
 static_assert(kTileKeys == kMaxTokens, "a tile is one LDS sort");
 constexpr int kRankSlice = kSortThreads;   // sorted keys per rank_kernel workgroup
 constexpr int kSumThreads = 256;           // chunk_sums_kernel workgroup
+constexpr int kSumTilesPerUnit = 4;        // column tiles of one chunk per chunk-sum unit
+constexpr int kSumGroupsPerCu = 32;        // chunk_sums_kernel workgroups per compute unit
 
 // Word per sorted rank: 0, or the first row of a chunk: bit 0 set, rows - 1
 // in bits 1..4, bit 5 if the run has more than 10 rows, bit 6 if the chunk is
-// the run's first.
+// the run's first; the first chunk of a long run carries the run's number of
+// combine tasks from bit 8 (at most ceil(hidden / 64) <= 2^18).
 constexpr uint32_t kHeadChunk = 1u, kHeadLong = 1u << 5, kHeadRun = 1u << 6;
+constexpr int kTasksShift = 8;
+constexpr uint32_t kHeadLongRun = kHeadChunk | kHeadLong | kHeadRun;
 
 __device__ __forceinline__ bool any_bad(const ManyHeader *hdr, int tiles, int32_t *sum) {
     int32_t s = 0;
@@ -78,40 +84,32 @@ __global__ __launch_bounds__(kSortThreads) void tile_sort_kernel(const IdT *__re
 
 // ---- 2. global ranks -------------------------------------------------------
 
-// Number of keys below `key` in each of the tiles, for `key_a` and `key_b`
-// at once: branch-free binary searches in lockstep (one step of every search
-// per round, so all their loads are in flight together).
-__device__ __forceinline__ void count_below(const uint32_t *__restrict__ tkeys, int n, int tiles,
-                                            uint32_t key_a, uint32_t key_b,
-                                            uint32_t (&below_a)[kManyMaxTiles],
-                                            uint32_t (&below_b)[kManyMaxTiles]) {
-#pragma unroll
-    for (int k = 0; k < kManyMaxTiles; ++k) below_a[k] = below_b[k] = 0u;
+// Keys of `a[0, nk)` (sorted) below `key`: branch-free binary search in LDS.
+__device__ __forceinline__ uint32_t lds_count_below(const uint32_t *a, uint32_t nk, uint32_t key) {
+    uint32_t below = 0u;
 #pragma unroll
     for (int b = kTileBits; b >= 0; --b) {
-        uint32_t va[kManyMaxTiles], vb[kManyMaxTiles];
-#pragma unroll
-        for (int k = 0; k < kManyMaxTiles; ++k) {
-            const int nk = n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys;
-            const uint32_t ca = below_a[k] + (1u << b), cb = below_b[k] + (1u << b);
-            va[k] = k < tiles && ca <= (uint32_t)nk ? tkeys[k * kTileKeys + ca - 1] : 0xffffffffu;
-            vb[k] = k < tiles && cb <= (uint32_t)nk ? tkeys[k * kTileKeys + cb - 1] : 0xffffffffu;
-        }
-#pragma unroll
-        for (int k = 0; k < kManyMaxTiles; ++k) {
-            if (va[k] < key_a) below_a[k] += 1u << b;
-            if (vb[k] < key_b) below_b[k] += 1u << b;
-        }
+        const uint32_t c = below + (1u << b);
+        if (c <= nk && a[c - 1] < key) below = c;
     }
+    return below;
 }
 
-__global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles,
+// Combine tasks of a long run of `len` rows: blocks of combine_width columns.
+__device__ __forceinline__ uint32_t run_tasks(uint32_t len, int hidden) {
+    const int chunks = (int)((len + kNRows - 1) / kNRows);
+    const int w = combine_width(chunks, hidden);
+    return (uint32_t)((hidden + w - 1) / w);
+}
+
+__global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles, int hidden,
                                                             const ManyHeader *__restrict__ hdr,
                                                             const uint32_t *__restrict__ tkeys,
                                                             int32_t *__restrict__ gpos,
                                                             uint32_t *__restrict__ gid,
                                                             uint32_t *__restrict__ cw,
                                                             uint32_t *__restrict__ glen) {
+    __shared__ uint32_t s_tile[2][kTileKeys];   // the tile being searched, the next one arriving
     __shared__ uint32_t s_res[3][kRankSlice];   // per id of the slice: before, run start, run length
     __shared__ uint64_t s_scan[kSortWaves + 1];
     int32_t bad;
@@ -127,17 +125,48 @@ __global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles,
     uint64_t heads;
     const uint32_t excl = (uint32_t)block_exclusive_scan(head ? 1u : 0u, s_scan, &heads);
     const uint32_t ord = head ? excl : excl - 1u;   // the slice's id groups in order
-    if (head) {
-        uint32_t lo[kManyMaxTiles], hi[kManyMaxTiles];
-        count_below(tkeys, n, tiles, x << kTileBits, (x + 1u) << kTileBits, lo, hi);
-        uint32_t before = 0u, start = 0u, len = 0u;
+
+    // Every tile in turn, staged in LDS (thread j moves keys [8j, 8j + 8));
+    // the loads of the next two tiles are in flight while one is searched.
+    // Each id group of the slice counts, in every tile k, the keys below x and
+    // below x + 1 (ids < x, ids <= x).
+    const uint32_t key_a = x << kTileBits, key_b = (x + 1u) << kTileBits;
+    uint32_t before = 0u, start = 0u, len = 0u;
+    auto fetch = [&](int k, uint4 (&r)[2]) {
+        const int nk = n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys;
+        const uint4 *src = reinterpret_cast<const uint4 *>(tkeys + (size_t)k * kTileKeys);
 #pragma unroll
-        for (int k = 0; k < kManyMaxTiles; ++k) {
-            start += lo[k];
-            len += hi[k] - lo[k];
-            if (k < t) before += hi[k];       // earlier positions of this id and smaller ids
-            else if (k > t) before += lo[k];  // smaller ids only
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid * kSortItems + 4 * q;   // first key of this piece
+            r[q] = e < nk ? src[e / 4] : uint4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
         }
+    };
+    // tile k: into LDS buffer k & 1 (last searched two tiles ago), then the
+    // registers refill with tile k + 2
+    auto step = [&](int k, uint4 (&r)[2]) {
+        uint4 *dst = reinterpret_cast<uint4 *>(s_tile[k & 1]);
+        dst[2 * tid] = r[0];
+        dst[2 * tid + 1] = r[1];
+        __syncthreads();
+        if (k + 2 < tiles) fetch(k + 2, r);
+        if (head) {
+            const uint32_t nk = (uint32_t)(n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys);
+            const uint32_t lo = lds_count_below(s_tile[k & 1], nk, key_a);
+            const uint32_t hi = lds_count_below(s_tile[k & 1], nk, key_b);
+            start += lo;
+            len += hi - lo;
+            if (k < t) before += hi;       // earlier positions of this id and smaller ids
+            else if (k > t) before += lo;  // smaller ids only
+        }
+    };
+    uint4 ra[2], rb[2];
+    fetch(0, ra);
+    if (tiles > 1) fetch(1, rb);
+    for (int k = 0; k < tiles; k += 2) {
+        step(k, ra);
+        if (k + 1 < tiles) step(k + 1, rb);   // uniform
+    }
+    if (head) {
         s_res[0][ord] = before;
         s_res[1][ord] = start;
         s_res[2][ord] = len;
@@ -145,29 +174,25 @@ __global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles,
     __syncthreads();
     if (!valid) return;
     const uint32_t rank = s_res[0][ord] + (uint32_t)i;
-    const uint32_t start = s_res[1][ord], len = s_res[2][ord];
+    const uint32_t run0 = s_res[1][ord], rlen = s_res[2][ord];
     if (rank >= (uint32_t)n) return;   // never: the ranks of the n keys are 0 .. n-1
-    const uint32_t off = rank - start;
+    const uint32_t off = rank - run0;
     gpos[rank] = t * kTileKeys + (int32_t)(key & (kTileKeys - 1));
     gid[rank] = x;
     uint32_t w = 0u;
     if (off % kNRows == 0) {
-        const uint32_t rows = len - off < (uint32_t)kNRows ? len - off : (uint32_t)kNRows;
-        w = kHeadChunk | ((rows - 1u) << 1) | (len > (uint32_t)kNRows ? kHeadLong : 0u) |
-            (off == 0 ? kHeadRun : 0u);
+        const uint32_t rows = rlen - off < (uint32_t)kNRows ? rlen - off : (uint32_t)kNRows;
+        w = kHeadChunk | ((rows - 1u) << 1) | (rlen > (uint32_t)kNRows ? kHeadLong : 0u);
+        if (off == 0) {
+            w |= kHeadRun;
+            if (rlen > (uint32_t)kNRows) w |= run_tasks(rlen, hidden) << kTasksShift;
+        }
     }
     cw[rank] = w;
-    if (off == 0) glen[rank] = len;
+    if (off == 0) glen[rank] = rlen;
 }
 
 // ---- 3. chunk and long-run lists -------------------------------------------
-
-// Combine tasks of a long run of `len` rows: blocks of combine_width columns.
-__device__ __forceinline__ uint32_t run_tasks(uint32_t len, int hidden) {
-    const int chunks = (int)((len + kNRows - 1) / kNRows);
-    const int w = combine_width(chunks, hidden);
-    return (uint32_t)((hidden + w - 1) / w);
-}
 
 // counters packed in 21-bit fields: chunks, long runs, long chunks
 __device__ __forceinline__ uint64_t head_counts(uint32_t w) {
@@ -178,7 +203,7 @@ __device__ __forceinline__ uint64_t head_counts(uint32_t w) {
 
 constexpr uint64_t kField = (1ull << 21) - 1;
 
-__global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int tiles, int hidden,
+__global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int tiles,
                                                                   uint32_t max_long_runs,
                                                                   uint32_t max_long_chunks,
                                                                   ManyHeader *__restrict__ hdr,
@@ -200,15 +225,24 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
     const int r0 = blockIdx.x * kTileKeys;
     // counts over the ranks of earlier blocks (each block recounts them: no
     // block waits for another)
+    // (r0 is a multiple of 8192: whole rounds of 4 x 1024 x 4 words, all
+    // loads of a round in flight together)
     uint64_t pre = 0, pre_tasks = 0;
-    for (int r = tid * 4; r < r0; r += kSortThreads * 4) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(cw + r);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    for (int r = tid * 4; r < r0; r += kSortThreads * 16) {
+        uint4 v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pre += head_counts(w4[j]);
-            if ((w4[j] & (kHeadChunk | kHeadLong | kHeadRun)) == (kHeadChunk | kHeadLong | kHeadRun))
-                pre_tasks += run_tasks(glen[r + j], hidden);
+        for (int q = 0; q < 4; ++q) {
+            const int rq = r + q * kSortThreads * 4;
+            v[q] = rq < r0 ? *reinterpret_cast<const uint4 *>(cw + rq) : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pre += head_counts(w4[j]);
+                if ((w4[j] & kHeadLongRun) == kHeadLongRun) pre_tasks += w4[j] >> kTasksShift;
+            }
         }
     }
     uint64_t base, base_tasks;
@@ -217,14 +251,30 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
 
     // this block's ranks: thread j owns [r0 + 8j, r0 + 8j + 8)
     const int s0 = r0 + tid * kSortItems;
-    uint32_t w[kSortItems];
+    // 16-byte loads of the thread's 8 words of each array, all in flight
+    // together (a piece past n reads workspace that follows the array: its
+    // words are masked below)
+    uint32_t w[kSortItems], ids8[kSortItems], len8[kSortItems];
     uint64_t mine = 0, mine_tasks = 0;
+    if (s0 < n) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(cw + s0 + 4 * q);
+            const uint4 b = *reinterpret_cast<const uint4 *>(gid + s0 + 4 * q);
+            const uint4 c = *reinterpret_cast<const uint4 *>(glen + s0 + 4 * q);
+            w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
+            ids8[4 * q] = b.x; ids8[4 * q + 1] = b.y; ids8[4 * q + 2] = b.z; ids8[4 * q + 3] = b.w;
+            len8[4 * q] = c.x; len8[4 * q + 1] = c.y; len8[4 * q + 2] = c.z; len8[4 * q + 3] = c.w;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
-        w[j] = s0 + j < n ? cw[s0 + j] : 0u;
+        if (s0 + j >= n) w[j] = ids8[j] = len8[j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
         mine += head_counts(w[j]);
-        if ((w[j] & (kHeadChunk | kHeadLong | kHeadRun)) == (kHeadChunk | kHeadLong | kHeadRun))
-            mine_tasks += run_tasks(glen[s0 + j], hidden);
+        if ((w[j] & kHeadLongRun) == kHeadLongRun) mine_tasks += w[j] >> kTasksShift;
     }
     uint64_t all, all_tasks;
     uint64_t idx = base + block_exclusive_scan(mine, s_scan, &all);
@@ -238,15 +288,15 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
             const uint32_t lc = (uint32_t)((idx >> 42) & kField);
             const bool lng = (w[j] & kHeadLong) != 0;
             const uint32_t rows = ((w[j] >> 1) & 15u) + 1u;
-            const uint32_t row = gid[s];
+            const uint32_t row = ids8[j];
             // (the bounds hold by construction: at most n chunks, n / 11 long
             // runs, 2n / 11 long-run chunks)
             if (c < (uint32_t)n && (!lng || lc < max_long_chunks))
                 chunks[c] = u32x4{s, rows, row, lng ? lc : 0xffffffffu};
             if (lng && (w[j] & kHeadRun) && lr < max_long_runs) {
-                const uint32_t len = glen[s];
+                const uint32_t len = len8[j];
                 runs[lr] = u32x4{row, lc, (len + kNRows - 1) / kNRows, (uint32_t)task};
-                task += run_tasks(len, hidden);
+                task += w[j] >> kTasksShift;
             }
             idx += head_counts(w[j]);
         }
@@ -263,6 +313,11 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
 
 // ---- 4. chunk sums ---------------------------------------------------------
 
+// Units are (chunk, group of kSumTilesPerUnit column tiles), chunk-major;
+// wave w of W takes units w, w + W, ... The grid holds several times more
+// workgroups than fit at once, so the hardware hands each compute unit a new
+// workgroup as one finishes: units of unequal cost even out without any
+// counter.
 template <typename G, typename M, int VEC>
 __global__ __launch_bounds__(kSumThreads) void chunk_sums_kernel(
     int n, int num_embeddings, const ManyHeader *__restrict__ hdr,
@@ -271,7 +326,7 @@ __global__ __launch_bounds__(kSumThreads) void chunk_sums_kernel(
     typename M::T *__restrict__ main_grad, int64_t mg_stride, float *__restrict__ partial,
     int64_t partial_stride, uint32_t max_long_chunks, int hidden, int tiles) {
     const uint32_t n_chunks = min(hdr->n_chunks, (uint32_t)n);
-    const uint32_t groups = (uint32_t)((tiles + kTilesPerUnit - 1) / kTilesPerUnit);
+    const uint32_t groups = (uint32_t)((tiles + kSumTilesPerUnit - 1) / kSumTilesPerUnit);
     const uint32_t units = n_chunks * groups;
     const int full_tiles = hidden / (64 * VEC);
     const uint32_t waves = gridDim.x * (kSumThreads / 64);
@@ -291,10 +346,10 @@ __global__ __launch_bounds__(kSumThreads) void chunk_sums_kernel(
 #pragma unroll
         for (int r = 0; r < kNRows; ++r) {
             const int32_t p = r < rows ? gpos[s + r] : 0;
-            pos[r] = p >= 0 && p < n ? p : 0;   // every row inside grad
+            pos[r] = __builtin_amdgcn_readfirstlane(p >= 0 && p < n ? p : 0);   // inside grad
         }
-        const int t0 = (int)g * kTilesPerUnit;
-        const int t_end = t0 + kTilesPerUnit < tiles ? t0 + kTilesPerUnit : tiles;
+        const int t0 = (int)g * kSumTilesPerUnit;
+        const int t_end = t0 + kSumTilesPerUnit < tiles ? t0 + kSumTilesPerUnit : tiles;
         chunk_tiles_any<G, M, VEC>(pos, rows, (int)row, dest == 0xffffffffu ? -1 : (int)dest,
                                    grad, grad_stride, main_grad, mg_stride, partial,
                                    partial_stride, hidden, t0, t_end, full_tiles);
@@ -354,11 +409,11 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int id_bits, const
     tile_sort_kernel<IdT><<<tiles, kSortThreads, 0, stream>>>(
         static_cast<const IdT *>(ids), n, num_embeddings, id_bits, hdr, tkeys);
     rank_kernel<<<tiles * (kTileKeys / kRankSlice), kSortThreads, 0, stream>>>(
-        n, tiles, hdr, tkeys, gpos, gid, cw, glen);
+        n, tiles, hidden, hdr, tkeys, gpos, gid, cw, glen);
     chunk_list_kernel<<<tiles, kSortThreads, 0, stream>>>(
-        n, tiles, hidden, (uint32_t)l.max_long_runs, (uint32_t)l.max_long_chunks, hdr, gid, cw, glen,
+        n, tiles, (uint32_t)l.max_long_runs, (uint32_t)l.max_long_chunks, hdr, gid, cw, glen,
         chunks, runs);
-    chunk_sums_kernel<G, M, VEC><<<num_cus * 8, kSumThreads, 0, stream>>>(
+    chunk_sums_kernel<G, M, VEC><<<num_cus * kSumGroupsPerCu, kSumThreads, 0, stream>>>(
         n, num_embeddings, hdr, chunks, gpos, static_cast<const typename G::T *>(grad),
         grad_stride, static_cast<typename M::T *>(main_grad), mg_stride, partial, l.partial_stride,
         (uint32_t)l.max_long_chunks, hidden, col_tiles);
