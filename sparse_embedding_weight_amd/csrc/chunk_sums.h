@@ -16,16 +16,18 @@
 namespace ewg {
 
 constexpr int kTilesPerUnit = 4;         // most column tiles of one chunk per unit / batch of loads
-constexpr int kStageFloats = 32768;      // combine staging: 128 KiB of chunk sums
+constexpr int kStageFloats = 32768;      // default combine staging: 128 KiB of chunk sums
 constexpr int kMaxCombineCols = 8192;    // columns of one combine block (8 per thread)
 
 // Columns of one combine task for a run of `chunks` chunk sums: the widest
-// multiple of 64 columns that lets the whole run fit the staging buffer, at
+// multiple of 64 columns that lets the whole run fit the staging buffer of
+// STAGE floats, at
 // least 64, at most kMaxCombineCols and at most hidden rounded up to 64. Deep
 // runs get narrow tasks (many in parallel, one load round trip each), shallow
 // runs one task for all columns.
+template <int STAGE = kStageFloats>
 __device__ __forceinline__ int combine_width(int chunks, int hidden) {
-    int w = kStageFloats / (chunks > 1 ? chunks : 1);
+    int w = STAGE / (chunks > 1 ? chunks : 1);
     w = w / 64 * 64;
     w = w < 64 ? 64 : (w > kMaxCombineCols ? kMaxCombineCols : w);
     const int h = (hidden + 63) / 64 * 64;
@@ -193,11 +195,11 @@ __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, i
 
 // One block of columns [col0, col0 + wdt) of a long run whose `chunks`
 // partial rows start at row `first` of the partial buffer, by all 1024
-// threads: the partial rows are staged in LDS (`stage`, kStageFloats floats),
+// threads: the partial rows are staged in LDS (`stage`, STAGE floats),
 // as many at a time as fit, and every column's running total adds them in
 // chunk order starting from +0; the total is then rounded once and added to
-// main_grad row `row`. wdt is combine_width(chunks, hidden).
-template <typename G, typename M>
+// main_grad row `row`. wdt is combine_width<STAGE>(chunks, hidden).
+template <typename G, typename M, int STAGE = kStageFloats>
 __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32_t first,
                                               uint32_t chunks, int64_t col0, int wdt,
                                               const float *__restrict__ partial,
@@ -219,7 +221,7 @@ __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32
     }
     const int quads = (wc + 3) / 4;           // 16-byte pieces of one chunk row
     // chunks per stage: the buffer, and a byte range below 2 GiB
-    int per_stage = kStageFloats / wdt;
+    int per_stage = STAGE / wdt;
     const int64_t by_range = ((int64_t)1 << 29) / partial_stride;
     if (per_stage > by_range) per_stage = (int)by_range;
     for (int k0 = 0; k0 < (int)chunks; k0 += per_stage) {
@@ -228,7 +230,7 @@ __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32
         const uint32_t range = (uint32_t)(((int64_t)(ks - 1) * partial_stride + 4 * quads) * 4);
         const __amdgpu_buffer_rsrc_t rs = buffer_range(base, range);
         const int pieces = ks * quads;
-        constexpr int kLoads = kStageFloats / 4 / kSortThreads;
+        constexpr int kLoads = STAGE / 4 / kSortThreads;
         u32x4 v[kLoads];
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {   // all loads in flight; past the range they read 0

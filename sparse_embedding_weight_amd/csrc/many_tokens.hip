@@ -49,7 +49,12 @@ static_assert(kTileKeys == kMaxTokens, "a tile is one LDS sort");
 constexpr int kRankSlice = kSortThreads;   // sorted keys per rank_kernel workgroup
 constexpr int kSumThreads = 256;           // chunk_sums_kernel workgroup
 constexpr int kSumTilesPerUnit = 4;        // column tiles of one chunk per chunk-sum unit
-constexpr int kSumGroupsPerCu = 32;        // chunk_sums_kernel workgroups per compute unit
+constexpr int kSumGroupsPerCu = 64;        // chunk_sums_kernel workgroups per compute unit
+// combine staging: 128 KiB, one workgroup per CU. (32 KiB, four per CU,
+// measured slower: a deep run's task then needs several staging round trips
+// in a row.)
+constexpr int kManyStage = kStageFloats;
+constexpr int kCombineGroupsPerCu = 4;     // combine_kernel workgroups per compute unit (one fits)
 
 // Word per sorted rank: 0, or the first row of a chunk: bit 0 set, rows - 1
 // in bits 1..4, bit 5 if the run has more than 10 rows, bit 6 if the chunk is
@@ -98,7 +103,7 @@ __device__ __forceinline__ uint32_t lds_count_below(const uint32_t *a, uint32_t 
 // Combine tasks of a long run of `len` rows: blocks of combine_width columns.
 __device__ __forceinline__ uint32_t run_tasks(uint32_t len, int hidden) {
     const int chunks = (int)((len + kNRows - 1) / kNRows);
-    const int w = combine_width(chunks, hidden);
+    const int w = combine_width<kManyStage>(chunks, hidden);
     return (uint32_t)((hidden + w - 1) / w);
 }
 
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(kSortThreads) void combine_kernel(
     int num_embeddings, const ManyHeader *__restrict__ hdr, const u32x4 *__restrict__ runs,
     const float *__restrict__ partial, int64_t partial_stride, typename M::T *__restrict__ main_grad,
     int64_t mg_stride, uint32_t max_long_chunks, uint32_t max_long_runs, int hidden) {
-    __shared__ float stage[kStageFloats];
+    __shared__ float stage[kManyStage];
     const uint32_t n_tasks = hdr->n_tasks;
     const int n_lr = (int)min(hdr->n_long_runs, max_long_runs);
     for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
@@ -375,13 +380,13 @@ __global__ __launch_bounds__(kSortThreads) void combine_kernel(
         }
         const u32x4 rec = runs[lo];
         const uint32_t row = rec.x, first = rec.y, chunks = rec.z;
-        const int wdt = combine_width((int)chunks, hidden);
+        const int wdt = combine_width<kManyStage>((int)chunks, hidden);
         const int64_t col0 = (int64_t)(t - rec.w) * wdt;
         // a record that does not describe this call's work (never expected) is skipped
         if (n_lr < 1 || rec.w > t || row >= (uint32_t)num_embeddings || chunks < 1 ||
             first >= max_long_chunks || chunks > max_long_chunks - first || col0 >= hidden)
             continue;
-        combine_block<G, M>(stage, row, first, chunks, col0, wdt, partial, partial_stride,
+        combine_block<G, M, kManyStage>(stage, row, first, chunks, col0, wdt, partial, partial_stride,
                             main_grad, mg_stride, hidden);
         __syncthreads();
     }
@@ -417,7 +422,7 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int id_bits, const
         n, num_embeddings, hdr, chunks, gpos, static_cast<const typename G::T *>(grad),
         grad_stride, static_cast<typename M::T *>(main_grad), mg_stride, partial, l.partial_stride,
         (uint32_t)l.max_long_chunks, hidden, col_tiles);
-    combine_kernel<G, M><<<num_cus, kSortThreads, 0, stream>>>(
+    combine_kernel<G, M><<<num_cus * kCombineGroupsPerCu, kSortThreads, 0, stream>>>(
         num_embeddings, hdr, runs, partial, l.partial_stride,
         static_cast<typename M::T *>(main_grad), mg_stride, (uint32_t)l.max_long_chunks,
         (uint32_t)l.max_long_runs, hidden);
