@@ -40,10 +40,12 @@
 // LDS counters and touches every shared counter about once per workgroup.
 // The flag is raised by workgroup 0, which waits for nothing before it; a
 // combine task waits only for the long units of the shares of other
-// workgroups, which wait for nothing but the flag, so every wait ends as long
-// as the launch's workgroups are resident together (one per compute unit, as
-// launched). Every wait is bounded; a wait that gives up is counted in the
-// workspace header and its work skipped.
+// workgroups, which wait for nothing but the flag. If such a wait lasts long
+// (200 us: some workgroups of the launch have not started, because more were
+// launched than fit or other work holds compute units), the waiting workgroup
+// claims the run's unclaimed shares and sums them itself, so every wait ends
+// whatever number of workgroups runs at once. Every wait is bounded; a wait
+// that gives up is counted in the workspace header and its work skipped.
 //
 // A column tile is 64 lanes x VEC columns (8 for bf16 grad, 4 for fp32), laid
 // out in lane-contiguous pieces (piece_cols in ewg_device.h).
