@@ -24,7 +24,7 @@
 //      length (keys with its id). Writes per rank: position, id, and a word
 //      that marks the first row of every chunk (chunks of 10 counted from the
 //      run's first rank) with its row count and whether the run is long.
-//   3. chunk_list_kernel (one workgroup per 8192 ranks): prefix counts of the
+//   3. chunk_list_kernel (one workgroup per 2048 ranks): prefix counts of the
 //      marked ranks give every chunk its record (first rank, rows, main_grad
 //      row, partial row for a chunk of a long run) and every long run its
 //      record (row, first partial row, chunk count, first combine task).
@@ -47,6 +47,8 @@ constexpr int kTileBits = 13;              // positions inside a tile
 constexpr int kTileKeys = 1 << kTileBits;  // keys one workgroup sorts
 static_assert(kTileKeys == kMaxTokens, "a tile is one LDS sort");
 constexpr int kRankSlice = kSortThreads;   // sorted keys per rank_kernel workgroup
+constexpr int kListItems = 2;              // ranks per thread of chunk_list_kernel
+constexpr int kListBlock = kSortThreads * kListItems;   // ranks per chunk_list_kernel workgroup
 constexpr int kSumThreads = 256;           // chunk_sums_kernel workgroup
 constexpr int kSumTilesPerUnit = 4;        // column tiles of one chunk per chunk-sum unit
 constexpr int kSumGroupsPerCu = 64;        // chunk_sums_kernel workgroups per compute unit
@@ -227,11 +229,10 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
         }
         return;
     }
-    const int r0 = blockIdx.x * kTileKeys;
+    const int r0 = blockIdx.x * kListBlock;
     // counts over the ranks of earlier blocks (each block recounts them: no
-    // block waits for another)
-    // (r0 is a multiple of 8192: whole rounds of 4 x 1024 x 4 words, all
-    // loads of a round in flight together)
+    // block waits for another); 16-byte loads, 4 per thread in flight
+    // together (r0 is a multiple of 4)
     uint64_t pre = 0, pre_tasks = 0;
     for (int r = tid * 4; r < r0; r += kSortThreads * 16) {
         uint4 v[4];
@@ -254,30 +255,27 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
     block_exclusive_scan(pre, s_scan, &base);
     block_exclusive_scan(pre_tasks, s_scan, &base_tasks);
 
-    // this block's ranks: thread j owns [r0 + 8j, r0 + 8j + 8)
-    const int s0 = r0 + tid * kSortItems;
-    // 16-byte loads of the thread's 8 words of each array, all in flight
-    // together (a piece past n reads workspace that follows the array: its
-    // words are masked below)
-    uint32_t w[kSortItems], ids8[kSortItems], len8[kSortItems];
+    // this block's ranks: thread j owns [r0 + 2j, r0 + 2j + 2); 8-byte loads
+    // of the thread's words of each array, all in flight together (a piece
+    // past n reads workspace that follows the array: its words are masked)
+    static_assert(kListItems == 2, "8-byte loads of two ranks");
+    const int s0 = r0 + tid * kListItems;
+    uint32_t w[kListItems] = {0u, 0u}, ids8[kListItems] = {0u, 0u}, len8[kListItems] = {0u, 0u};
     uint64_t mine = 0, mine_tasks = 0;
     if (s0 < n) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(cw + s0 + 4 * q);
-            const uint4 b = *reinterpret_cast<const uint4 *>(gid + s0 + 4 * q);
-            const uint4 c = *reinterpret_cast<const uint4 *>(glen + s0 + 4 * q);
-            w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
-            ids8[4 * q] = b.x; ids8[4 * q + 1] = b.y; ids8[4 * q + 2] = b.z; ids8[4 * q + 3] = b.w;
-            len8[4 * q] = c.x; len8[4 * q + 1] = c.y; len8[4 * q + 2] = c.z; len8[4 * q + 3] = c.w;
-        }
+        const uint2 a = *reinterpret_cast<const uint2 *>(cw + s0);
+        const uint2 b = *reinterpret_cast<const uint2 *>(gid + s0);
+        const uint2 c = *reinterpret_cast<const uint2 *>(glen + s0);
+        w[0] = a.x; w[1] = a.y;
+        ids8[0] = b.x; ids8[1] = b.y;
+        len8[0] = c.x; len8[1] = c.y;
     }
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kListItems; ++j) {
         if (s0 + j >= n) w[j] = ids8[j] = len8[j] = 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kListItems; ++j) {
         mine += head_counts(w[j]);
         if ((w[j] & kHeadLongRun) == kHeadLongRun) mine_tasks += w[j] >> kTasksShift;
     }
@@ -285,7 +283,7 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
     uint64_t idx = base + block_exclusive_scan(mine, s_scan, &all);
     uint64_t task = base_tasks + block_exclusive_scan(mine_tasks, s_scan, &all_tasks);
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kListItems; ++j) {
         if (w[j] & kHeadChunk) {
             const uint32_t s = (uint32_t)(s0 + j);
             const uint32_t c = (uint32_t)(idx & kField);
@@ -415,7 +413,7 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int id_bits, const
         static_cast<const IdT *>(ids), n, num_embeddings, id_bits, hdr, tkeys);
     rank_kernel<<<tiles * (kTileKeys / kRankSlice), kSortThreads, 0, stream>>>(
         n, tiles, hidden, hdr, tkeys, gpos, gid, cw, glen);
-    chunk_list_kernel<<<tiles, kSortThreads, 0, stream>>>(
+    chunk_list_kernel<<<(n + kListBlock - 1) / kListBlock, kSortThreads, 0, stream>>>(
         n, tiles, (uint32_t)l.max_long_runs, (uint32_t)l.max_long_chunks, hdr, gid, cw, glen,
         chunks, runs);
     chunk_sums_kernel<G, M, VEC><<<num_cus * kSumGroupsPerCu, kSumThreads, 0, stream>>>(
