@@ -216,3 +216,15 @@ def test_many_tokens_python_predicate():
     assert not ewg.can_accumulate_embedding_wgrad_many_tokens(ids, grad, mg)
     with pytest.raises(ValueError):
         ewg.accumulate_embedding_wgrad_many_tokens(ids, grad, mg)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path needs no collective and is not sharded here: N > 1 exits with a message
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
