@@ -31,7 +31,11 @@
  *     non-zero return nothing was enqueued and main_grad is untouched
  *     (except EWG_HIP_ERROR, which reports a failed launch);
  *   - the functions are thread-safe; concurrent calls must not share a
- *     workspace unless ordered by their streams.
+ *     workspace unless ordered by their streams;
+ *   - the accumulate entry points enqueue kernels only (no memset, no copy,
+ *     no allocation), so a call can be captured in a HIP graph and the graph
+ *     replayed: each replay adds the gradient again, exactly as a new call
+ *     with the same arguments would.
  */
 #ifndef EMBEDDING_WGRAD_H
 #define EMBEDDING_WGRAD_H
