@@ -163,10 +163,15 @@ int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_gra
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * accumulate_embedding_wgrad with timing markers: `events` points to 2
- * caller-created hipEvent_t, recorded on `stream` right before and right
- * after the kernel. Same arguments, results and errors otherwise; meant for
- * benchmarks.
+ * accumulate_embedding_wgrad with timing markers: `events` points to 4
+ * caller-created hipEvent_t (timing enabled). events[0] and events[1] are
+ * recorded on `stream` right before and right after the call's work;
+ * events[2] and events[3] are attached to the kernel's own dispatch
+ * (hipExtLaunchKernelGGL), so that they span the kernel's execution alone.
+ * events[2] and events[3] may both be NULL: the kernel is then dispatched as
+ * in accumulate_embedding_wgrad (such a dispatch costs less time around the
+ * kernel than one that takes events). Same arguments, results and errors
+ * otherwise; meant for benchmarks.
  */
 int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *main_grad,
                                      int64_t num_tokens, int64_t hidden, int64_t num_embeddings,

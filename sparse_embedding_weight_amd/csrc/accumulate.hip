@@ -49,6 +49,8 @@
 //
 // A column tile is 64 lanes x VEC columns (8 for bf16 grad, 4 for fp32), laid
 // out in lane-contiguous pieces (piece_cols in ewg_device.h).
+#include <hip/hip_ext.h>
+
 #include "chunk_sums.h"
 #include "ewg_device.h"
 #include "ewg_internal.h"
@@ -772,17 +774,31 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, i
                   int pos_bits, int id_bits,
                   const void *grad, int64_t grad_stride, void *main_grad, int64_t mg_stride,
                   int hidden, void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                  int defer_odd_shares, hipStream_t stream) {
+                  int defer_odd_shares, hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     const int tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
     const int grid = num_cus < 2 ? 2 : (num_cus > kMaxGrid ? kMaxGrid : num_cus);
-    accumulate_kernel<IdT, G, M, VEC><<<grid, kSortThreads, 0, stream>>>(
-        static_cast<const IdT *>(ids), n, num_embeddings, id_base, skip_outside, pos_bits, id_bits,
-        static_cast<const typename G::T *>(grad), grad_stride,
-        static_cast<typename M::T *>(main_grad), mg_stride, hidden, tiles,
-        reinterpret_cast<WsHeader *>(ws), reinterpret_cast<uint8_t *>(ws + l.units), reinterpret_cast<uint8_t *>(ws + l.runs),
-        reinterpret_cast<uint32_t *>(ws + l.done), reinterpret_cast<uint32_t *>(ws + l.shares),
-        reinterpret_cast<float *>(ws + l.partial), l.partial_stride, epoch, defer_odd_shares);
+    auto kernel = accumulate_kernel<IdT, G, M, VEC>;
+    const IdT *ids_t = static_cast<const IdT *>(ids);
+    const typename G::T *grad_t = static_cast<const typename G::T *>(grad);
+    typename M::T *mg_t = static_cast<typename M::T *>(main_grad);
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws);
+    uint8_t *units = reinterpret_cast<uint8_t *>(ws + l.units);
+    uint8_t *runs = reinterpret_cast<uint8_t *>(ws + l.runs);
+    uint32_t *done = reinterpret_cast<uint32_t *>(ws + l.done);
+    uint32_t *shares = reinterpret_cast<uint32_t *>(ws + l.shares);
+    float *partial = reinterpret_cast<float *>(ws + l.partial);
+    if (kstart && kstop)   // events taken by the dispatch itself: the kernel's own duration
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kSortThreads), 0, stream, kstart, kstop, 0,
+                              ids_t, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits,
+                              grad_t, grad_stride, mg_t, mg_stride, hidden, tiles, hdr, units, runs,
+                              done, shares, partial, l.partial_stride, epoch, defer_odd_shares);
+    else
+        kernel<<<grid, kSortThreads, 0, stream>>>(ids_t, n, num_embeddings, id_base, skip_outside,
+                                                  pos_bits, id_bits, grad_t, grad_stride, mg_t,
+                                                  mg_stride, hidden, tiles, hdr, units, runs, done,
+                                                  shares, partial, l.partial_stride, epoch,
+                                                  defer_odd_shares);
     return hipGetLastError();
 }
 
@@ -792,11 +808,12 @@ hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *id
                           int id_bits, const void *grad,
                           int64_t grad_stride, void *main_grad, int64_t mg_stride, int hidden,
                           void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                          int defer_odd_shares, hipStream_t stream) {
+                          int defer_odd_shares, hipEvent_t kstart, hipEvent_t kstop,
+                          hipStream_t stream) {
 #define EWG_ACC(G, M, V)                                                                        \
     launch<IdT, G, M, V>(ids, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits, grad,   \
-                         grad_stride, main_grad,                                                  \
-                         mg_stride, hidden, workspace, l, num_cus, epoch, defer_odd_shares, stream)
+                         grad_stride, main_grad, mg_stride, hidden, workspace, l, num_cus, epoch, \
+                         defer_odd_shares, kstart, kstop, stream)
     if (grad_bf16) {
         if (mg_bf16) return vec ? EWG_ACC(BF16, BF16, 8) : EWG_ACC(BF16, BF16, 1);
         return vec ? EWG_ACC(BF16, F32, 8) : EWG_ACC(BF16, F32, 1);
@@ -814,14 +831,16 @@ hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool 
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
                              int num_cus, uint32_t epoch, int defer_odd_shares,
-                             hipStream_t stream) {
+                             hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream) {
     if (ids_int64)
         return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
-                                       skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
-                                       workspace, l, num_cus, epoch, defer_odd_shares, stream);
+                                       skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride,
+                                       main_grad, mg_stride, hidden, workspace, l, num_cus, epoch,
+                                       defer_odd_shares, kstart, kstop, stream);
     return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
-                                   skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride, main_grad, mg_stride, hidden,
-                                   workspace, l, num_cus, epoch, defer_odd_shares, stream);
+                                   skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride,
+                                   main_grad, mg_stride, hidden, workspace, l, num_cus, epoch,
+                                   defer_odd_shares, kstart, kstop, stream);
 }
 
 }  // namespace ewg

@@ -146,6 +146,7 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                                      grad_row_stride,
                                      main_grad, main_grad_row_stride, (int)hidden, workspace, l,
                                      launch_grid(num_cus()), next_epoch(), defer_odd_shares(),
+                                     events ? events[2] : nullptr, events ? events[3] : nullptr,
                                      stream));
     if (st != EWG_OK) return st;
     if (events && hipEventRecord(events[1], stream) != hipSuccess) return EWG_HIP_ERROR;

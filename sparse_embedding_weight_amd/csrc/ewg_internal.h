@@ -185,6 +185,6 @@ hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool 
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
                              int num_cus, uint32_t epoch, int defer_odd_shares,
-                             hipStream_t stream);
+                             hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream);
 
 }  // namespace ewg
