@@ -21,11 +21,14 @@
 //      and finishes its equal-cost share of the runs of at most 10 rows (a run
 //      of at most 10 rows is one chunk: it needs its rows in position order,
 //      not a global sort).
-//   3. Each wave that is done waits for the flag; then every workgroup takes
-//      a fixed share of the (long chunk, column tile) units, stores their fp32
-//      chunk sums in the partial buffer with device-coherent stores and, once
-//      they have completed, adds its count of each run's units to that run's
-//      counter for its group of workgroups.
+//   3. The first wave of a workgroup to be done with its short runs waits
+//      for the flag, claims the workgroup's fixed share of the (long chunk,
+//      column tile) units and stages its records in LDS; every wave takes
+//      units as soon as it is done with its short runs and that is staged
+//      (no barrier in between), stores their fp32 chunk sums in the partial
+//      buffer with device-coherent stores and, once all have completed, the
+//      workgroup adds its count of each run's units to that run's counter for
+//      its group of workgroups.
 //   4. Then whole workgroups take combine tasks (one long run, one block of
 //      columns) from a ticket counter: wait until the run's units are all
 //      counted, stage its chunk sums in LDS, add them in chunk order from +0,
@@ -94,8 +97,12 @@ struct LongSmem {
     u32x4 rec[2 * kMaxLongChunks];      // unit records of this workgroup's chunks, two halves each
     uint32_t run_cnt[kMaxLongRuns];     // units of each long run this workgroup has finished
     uint32_t claim;                     // next unit of this workgroup's share to claim
-    uint32_t won;                       // the share's slot was claimed by this workgroup
 };
+// A wave may stage a long share while its siblings still take short-run units
+// of their last round, which read only the run tables after the hash table:
+// the long share's LDS must lie inside the (then unused) hash keys.
+static_assert(sizeof(LongSmem) <= sizeof(uint32_t) * kHashSlots, "long share overlaps live LDS");
+static_assert(offsetof(FollowerSmem, key) == 0, "hash keys first");
 
 union AccSmem {
     SortSmem sort;
@@ -467,50 +474,107 @@ __device__ __forceinline__ bool claim_share(uint32_t *__restrict__ shares, uint3
                                                 __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Words of the long-unit hand-off, outside the LDS union: kLongElect holds
+// the number of the last long_units call whose staging wave was elected;
+// kLongState = call number << 2 | kStateNoFlag | kStateNoShare, published by
+// the staging wave; kLongChunks / kLongRuns the published counts.
+constexpr int kLongElect = 0, kLongState = 1, kLongChunks = 2, kLongRuns = 3;
+constexpr uint32_t kStateNoFlag = 1u, kStateNoShare = 2u;
+
 // Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
 // takes units [w * U / W, (w + 1) * U / W) of the U = chunks * tiles units:
 // the shares are fixed by the published chunk count alone, so no device-wide
 // counter is touched while the units run (a device-scope atomic in a wave
-// also holds back that wave's next loads until it returns). The records of
-// the share's chunks are copied to LDS, then the waves claim units one at a
-// time with an LDS counter. Each unit's fp32 chunk sums go to its partial
-// row with device-coherent stores. The finished units are counted per run
-// in LDS and added to the run's counter of this workgroup's group once,
-// after all stores of the workgroup have completed.
+// also holds back that wave's next loads until it returns).
+//
+// The waves enter one by one (after their short runs, on the first call) and
+// the first to enter stages the share for all: on the first call it waits for
+// the flag and loads the published counts; it claims the share's slot (mark 1
+// for the workgroup's own share, 2 for a take-over, 0 to leave the share
+// alone), copies the records of the share's chunks to LDS while the claim is
+// in flight, and publishes the outcome in `s_long`. The other waves wait for
+// that on LDS, not at a barrier, so a wave that is done with its short runs
+// starts long units while its siblings still finish theirs. The waves then
+// claim units one at a time with an LDS counter; each unit's fp32 chunk sums
+// go to its partial row with device-coherent stores. The finished units are
+// counted per run in LDS and added to the run's counter of this workgroup's
+// group once, after all stores of the workgroup have completed. `call` is the
+// number of this call in the workgroup (1, 2, ...; the same in every wave).
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t share, uint32_t mark,
+__device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint32_t call,
+                                           bool first_call, uint32_t share, uint32_t mark,
                                            uint32_t *__restrict__ shares, WsHeader *__restrict__ hdr,
                                            __amdgpu_buffer_rsrc_t units_rs,
-                                           uint32_t *__restrict__ done, uint32_t n_lc,
-                                           uint32_t n_lr, int n,
-                                           const typename G::T *__restrict__ grad,
+                                           uint32_t *__restrict__ done, uint32_t n_lc_in,
+                                           uint32_t n_lr_in, uint32_t n_lc_max, uint32_t n_lr_max,
+                                           int n, const typename G::T *__restrict__ grad,
                                            int64_t grad_stride, float *__restrict__ partial,
                                            int64_t partial_stride, int hidden, int tiles,
                                            uint32_t epoch) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int full_tiles = hidden / (64 * VEC);
+    // every branch below is on a wave-uniform value; the single-lane LDS
+    // updates are whole-wave atomics in which only lane 0 changes anything
+    const uint32_t one = lane == 0 ? 1u : 0u;
+    const uint32_t prev = call - 1u;
+    const bool stager = __builtin_amdgcn_readfirstlane(
+                            atomicCAS(&s_long[kLongElect], prev, lane == 0 ? call : prev)) == prev;
+    if (stager) {
+        bool ok = true;
+        uint32_t lc = n_lc_in, lr = n_lr_in;
+        if (first_call) {
+            ok = wave_wait_ready(hdr, epoch);
+            if (ok) {
+                lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
+                lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
+            }
+        }
+        lc = __builtin_amdgcn_readfirstlane(lc);
+        lr = __builtin_amdgcn_readfirstlane(lr);
+        bool won = false;
+        if (ok && mark != 0u) {
+            const uint32_t total = lc * (uint32_t)tiles;
+            const uint32_t lo = share_begin(total, share), hi = share_begin(total, share + 1);
+            const uint32_t c_lo = lo / (uint32_t)tiles;
+            const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;
+            // the claim is in flight together with the loads of the records
+            uint32_t w = 0u;
+            if (lane == 0) w = claim_share(shares, share, mark) ? 1u : 0u;
+            for (uint32_t i = (uint32_t)lane; i < 2 * (c_hi - c_lo); i += 64)
+                ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
+            for (uint32_t r = (uint32_t)lane; r < lr; r += 64) ls.run_cnt[r] = 0u;
+            if (lane == 0) ls.claim = 0u;
+            won = __builtin_amdgcn_readfirstlane(w) != 0u;
+        }
+        if (lane == 0) {
+            s_long[kLongChunks] = lc;
+            s_long[kLongRuns] = lr;
+        }
+        const uint32_t state = call << 2 | (ok ? 0u : kStateNoFlag) | (won ? 0u : kStateNoShare);
+        // the records, counters and counts above are visible before the state
+        __hip_atomic_store(&s_long[kLongState], state, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    uint32_t state;
+    int64_t spins = 0;
+    for (;;) {
+        state = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&s_long[kLongState], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if ((state >> 2) == call) break;
+        // the staging wave waits at most kWaitLimit polls of the flag and a few loads
+        if (++spins > 16 * kWaitLimit) {
+            if (lane == 0) fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+            state = call << 2 | kStateNoFlag;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (state & (kStateNoFlag | kStateNoShare)) return false;   // uniform over the workgroup
+
+    const uint32_t n_lc = s_long[kLongChunks], n_lr = s_long[kLongRuns];
     const uint32_t total = n_lc * (uint32_t)tiles;
     const uint32_t lo = share_begin(total, share);
     const uint32_t hi = share_begin(total, share + 1);
     const uint32_t c_lo = lo / (uint32_t)tiles;
-    const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;   // chunks [c_lo, c_hi)
-    // claim the share (its slot from 0 to `mark`) while its records are
-    // fetched, so that both round trips overlap; mark 0: the caller holds it
-    bool won = true;
-    if (tid == 0 && mark != 0u) won = claim_share(shares, share, mark);
-    for (uint32_t i = (uint32_t)tid; i < 2 * (c_hi - c_lo); i += kSortThreads)
-        ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
-    for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) ls.run_cnt[r] = 0u;
-    if (tid == 0) {
-        ls.claim = 0u;
-        ls.won = won ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!ls.won) return false;   // uniform: the share is someone else's
-
-    // every branch below is on a wave-uniform value; the single-lane LDS
-    // updates are whole-wave atomics in which only lane 0 adds anything
-    const uint32_t one = lane == 0 ? 1u : 0u;
     for (;;) {
         const uint32_t u = lo + __builtin_amdgcn_readfirstlane(atomicAdd(&ls.claim, one));
         if (u >= hi) break;
@@ -685,59 +749,55 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     float *__restrict__ partial, int64_t partial_stride, uint32_t epoch, int defer_odd_shares) {
     __shared__ AccSmem sm;
     __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
+    __shared__ uint32_t s_long[4];   // long-share hand-off (kLongElect ...)
     const int tid = threadIdx.x;
     const uint32_t n_lc_max = (uint32_t)(2 * n / 11), n_lr_max = (uint32_t)(n / 11);
     const __amdgpu_buffer_rsrc_t units_rs = buffer_range(units, n_lc_max * (uint32_t)kUnitRecordBytes);
     const __amdgpu_buffer_rsrc_t runs_rs = buffer_range(runs, n_lr_max * (uint32_t)kRunRecordBytes);
-    if (tid == 0) s_word[0] = 0u;   // set by waves that gave up on the flag; read after barriers
+    if (tid == 0) {   // read after the barriers of either first phase
+        s_long[kLongElect] = 0u;
+        s_long[kLongState] = 0u;
+    }
 
-    bool ready = true;
     if (blockIdx.x == 0) {
         leader_publish<IdT>(sm.sort, ids, n, num_embeddings, id_base, skip_outside != 0, pos_bits,
                             id_bits, hidden, hdr,
                             units_rs, runs_rs, done, shares, epoch);
     } else {
+        // the waves leave this one by one, as their short-run units run out
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
                                             skip_outside != 0, grad, grad_stride,
                                             main_grad, mg_stride, hidden, tiles,
                                             (int)blockIdx.x - 1, (int)gridDim.x - 1);
-        ready = wave_wait_ready(hdr, epoch);
     }
-    // all waves of the workgroup are past their short runs and the flag
-    if (!ready && (tid & 63) == 0) atomicOr(&s_word[0], 1u);
-    __syncthreads();
-    // shares [w, w_end) to process next, claimed with `mark` (0: already held)
-    uint32_t w = 0u, w_end = 0u, mark = 0u;
+    // Phases 3 and 4: the workgroup's own share (claimed with mark 1, unless a
+    // waiting combine task took it already; a test setting leaves every other
+    // share to the combine tasks: mark 0), then combine tasks. A combine task
+    // that waits long hands back the shares [w, w_end) its run still needs,
+    // taken over here with mark 2 (one copy of the long-unit code serves both).
+    uint32_t w = blockIdx.x, w_end = blockIdx.x + 1u;
+    uint32_t mark = defer_odd_shares && (blockIdx.x & 1u) ? 0u : 1u;
+    uint32_t call = 0u;
+    bool flag_seen = false;
     CombineCursor cur;
     cur.have_task = false;
     cur.task = 0u;
     cur.spins = 0;
     cur.n_lc = cur.n_lr = 0u;
-    if (s_word[0] == 0u) {   // uniform: every wave saw the flag
-        // this workgroup's own share, unless a waiting combine task took it already
-        // (a test setting leaves every other share to the combine tasks); the
-        // claim is in flight together with the loads of the counts
-        if (tid == 0)
-            s_word[1] = !(defer_odd_shares && (blockIdx.x & 1u)) && claim_share(shares, blockIdx.x, 1u);
-        cur.n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
-        cur.n_lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
-        __syncthreads();
-        if (s_word[1]) {
-            w = blockIdx.x;
-            w_end = w + 1u;
-        }
-    }
-    const bool flag_seen = s_word[0] == 0u;
-    __syncthreads();
-    // phases 3 and 4: the own share, then combine tasks; a combine task that
-    // waits long hands back the shares its run still needs, taken over here
-    // (one copy of the long-unit code serves both)
     for (;;) {
         for (; w < w_end; ++w) {
-            const bool took = long_units<G, M, VEC>(sm.lng, w, mark, shares, hdr, units_rs, done,
-                                                    cur.n_lc, cur.n_lr, n, grad, grad_stride,
-                                                    partial, partial_stride, hidden, tiles, epoch);
-            if (took && mark != 0u && tid == 0)
+            ++call;
+            const bool took = long_units<G, M, VEC>(sm.lng, s_long, call, call == 1u, w, mark,
+                                                    shares, hdr, units_rs, done, cur.n_lc,
+                                                    cur.n_lr, n_lc_max, n_lr_max, n, grad,
+                                                    grad_stride, partial, partial_stride, hidden,
+                                                    tiles, epoch);
+            if (call == 1u) {   // the flag and the counts, as the staging wave saw them
+                flag_seen = (s_long[kLongState] & kStateNoFlag) == 0u;
+                cur.n_lc = s_long[kLongChunks];
+                cur.n_lr = s_long[kLongRuns];
+            }
+            if (took && mark == 2u && tid == 0)
                 fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);
             __syncthreads();
         }
