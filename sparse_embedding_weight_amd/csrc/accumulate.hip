@@ -438,17 +438,31 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
 
 // ---- phase 3: chunks of long runs ---------------------------------------------
 
-// Wave-level wait for this call's flag; false if the wait gave up.
-__device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint32_t epoch) {
+// Wave-level wait for this call's flag; false if the wait gave up. The flag
+// and the published long-chunk and long-run counts are read by one 16-byte
+// load: the counts had completed before the flag was stored, so the load that
+// sees the flag returns them too.
+__device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint32_t epoch,
+                                                uint32_t *n_lc, uint32_t *n_lr) {
+    static_assert(offsetof(WsHeader, ready) % 16 == 0 &&
+                      offsetof(WsHeader, pub_long_chunks) == offsetof(WsHeader, ready) + 8 &&
+                      offsetof(WsHeader, pub_long_runs) == offsetof(WsHeader, ready) + 12,
+                  "flag and counts in one 16-byte word");
+    const __amdgpu_buffer_rsrc_t h = buffer_range(hdr, (uint32_t)sizeof(WsHeader));
     int64_t spins = 0;
-    while (__builtin_amdgcn_readfirstlane(load_coherent(&hdr->ready)) != epoch) {
+    for (;;) {
+        const u32x4 v = load_coherent16(h, (uint32_t)offsetof(WsHeader, ready));
+        if (__builtin_amdgcn_readfirstlane(v.x) == epoch) {
+            *n_lc = __builtin_amdgcn_readfirstlane(v.z);
+            *n_lr = __builtin_amdgcn_readfirstlane(v.w);
+            return true;
+        }
         __builtin_amdgcn_s_sleep(2);
         if (++spins > kWaitLimit) {
             if ((threadIdx.x & 63) == 0) fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
             return false;
         }
     }
-    return true;
 }
 
 // First long unit of share w of the launch's gridDim.x shares of `total`.
@@ -523,11 +537,9 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint3
         bool ok = true;
         uint32_t lc = n_lc_in, lr = n_lr_in;
         if (first_call) {
-            ok = wave_wait_ready(hdr, epoch);
-            if (ok) {
-                lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
-                lr = min(load_coherent(&hdr->pub_long_runs), n_lr_max);
-            }
+            ok = wave_wait_ready(hdr, epoch, &lc, &lr);
+            lc = min(lc, n_lc_max);
+            lr = min(lr, n_lr_max);
         }
         lc = __builtin_amdgcn_readfirstlane(lc);
         lr = __builtin_amdgcn_readfirstlane(lr);
