@@ -111,7 +111,7 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
  * workgroups run together, and the result is the same either way).
  * 0 if the sizes are out of range.
  */
-#define EWG_WS_WAIT_TIMEOUTS_OFFSET 132
+#define EWG_WS_WAIT_TIMEOUTS_OFFSET 144
 #define EWG_WS_STOLEN_SHARES_OFFSET 148
 
 size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);

@@ -336,7 +336,7 @@ def invalid_id_count(workspace: torch.Tensor) -> int:
     return int(workspace[:4].view(torch.int32).item())
 
 
-WS_WAIT_TIMEOUTS_OFFSET = 132   # EWG_WS_WAIT_TIMEOUTS_OFFSET
+WS_WAIT_TIMEOUTS_OFFSET = 144   # EWG_WS_WAIT_TIMEOUTS_OFFSET
 WS_STOLEN_SHARES_OFFSET = 148   # EWG_WS_STOLEN_SHARES_OFFSET
 
 

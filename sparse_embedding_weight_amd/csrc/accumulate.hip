@@ -102,6 +102,8 @@ struct LongSmem {
 // of their last round, which read only the run tables after the hash table:
 // the long share's LDS must lie inside the (then unused) hash keys.
 static_assert(sizeof(LongSmem) <= sizeof(uint32_t) * kHashSlots, "long share overlaps live LDS");
+// a take-over between two combine tasks keeps the run records staged for them
+static_assert(sizeof(LongSmem) <= offsetof(CombineSmem, runs), "long share overlaps the run records");
 static_assert(offsetof(FollowerSmem, key) == 0, "hash keys first");
 
 union AccSmem {
@@ -439,12 +441,13 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
 // ---- phase 3: chunks of long runs ---------------------------------------------
 
 // Wave-level wait for this call's flag; false if the wait gave up. The flag
-// and the published long-chunk and long-run counts are read by one 16-byte
-// load: the counts had completed before the flag was stored, so the load that
-// sees the flag returns them too.
+// and the published counts (combine tasks, long chunks, long runs) are read by
+// one 16-byte load: the counts had completed before the flag was stored, so
+// the load that sees the flag returns them too.
 __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint32_t epoch,
-                                                uint32_t *n_lc, uint32_t *n_lr) {
+                                                uint32_t *n_tasks, uint32_t *n_lc, uint32_t *n_lr) {
     static_assert(offsetof(WsHeader, ready) % 16 == 0 &&
+                      offsetof(WsHeader, pub_tasks) == offsetof(WsHeader, ready) + 4 &&
                       offsetof(WsHeader, pub_long_chunks) == offsetof(WsHeader, ready) + 8 &&
                       offsetof(WsHeader, pub_long_runs) == offsetof(WsHeader, ready) + 12,
                   "flag and counts in one 16-byte word");
@@ -453,6 +456,7 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     for (;;) {
         const u32x4 v = load_coherent16(h, (uint32_t)offsetof(WsHeader, ready));
         if (__builtin_amdgcn_readfirstlane(v.x) == epoch) {
+            *n_tasks = __builtin_amdgcn_readfirstlane(v.y);
             *n_lc = __builtin_amdgcn_readfirstlane(v.z);
             *n_lr = __builtin_amdgcn_readfirstlane(v.w);
             return true;
@@ -491,8 +495,9 @@ __device__ __forceinline__ bool claim_share(uint32_t *__restrict__ shares, uint3
 // Words of the long-unit hand-off, outside the LDS union: kLongElect holds
 // the number of the last long_units call whose staging wave was elected;
 // kLongState = call number << 2 | kStateNoFlag | kStateNoShare, published by
-// the staging wave; kLongChunks / kLongRuns the published counts.
-constexpr int kLongElect = 0, kLongState = 1, kLongChunks = 2, kLongRuns = 3;
+// the staging wave; kLongChunks / kLongRuns / kLongTasks the published counts.
+constexpr int kLongElect = 0, kLongState = 1, kLongChunks = 2, kLongRuns = 3, kLongTasks = 4;
+constexpr int kLongWords = 5;
 constexpr uint32_t kStateNoFlag = 1u, kStateNoShare = 2u;
 
 // Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
@@ -535,11 +540,12 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint3
                             atomicCAS(&s_long[kLongElect], prev, lane == 0 ? call : prev)) == prev;
     if (stager) {
         bool ok = true;
-        uint32_t lc = n_lc_in, lr = n_lr_in;
+        uint32_t lc = n_lc_in, lr = n_lr_in, nt = 0u;
         if (first_call) {
-            ok = wave_wait_ready(hdr, epoch, &lc, &lr);
+            ok = wave_wait_ready(hdr, epoch, &nt, &lc, &lr);
             lc = min(lc, n_lc_max);
             lr = min(lr, n_lr_max);
+            if (lane == 0) s_long[kLongTasks] = nt;
         }
         lc = __builtin_amdgcn_readfirstlane(lc);
         lr = __builtin_amdgcn_readfirstlane(lr);
@@ -634,7 +640,8 @@ struct CombineCursor {
     uint32_t task;        // the task being waited for, if have_task
     bool have_task;
     int64_t spins;        // polls spent on that task's wait
-    uint32_t n_lc, n_lr;  // the published long-chunk and long-run counts
+    uint32_t n_lc, n_lr, n_tasks;   // the published counts, as the flag's load returned them
+    bool runs_loaded;     // the run records are in LDS (nothing else writes that part later)
 };
 
 // Returns false once no combine task is left. Returns true, with the task
@@ -655,21 +662,16 @@ __device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, Com
                                               uint32_t n_lr_max) {
     CombineSmem &cs = sm.comb;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        const uint32_t lr = load_coherent(&hdr->pub_long_runs);
-        s_word[0] = lr < n_lr_max ? lr : n_lr_max;
-        s_word[1] = load_coherent(&hdr->pub_tasks);
-    }
-    __syncthreads();
-    const int n_lr = (int)s_word[0];
-    const uint32_t n_tasks = s_word[1];
+    // The counts are those the flag's load returned (without the flag, which
+    // never fails to come, there is no task to take). A workgroup takes a
+    // ticket first and loads the run records only for its first task, so
+    // one that finds the tasks gone leaves after one round trip.
+    if (!flag_seen) return false;
+    const int n_lr = (int)min(cur.n_lr, n_lr_max);
+    const uint32_t n_tasks = cur.n_tasks;
     if (n_lr == 0 || n_tasks == 0) return false;   // uniform
-    const uint32_t n_lc = min(load_coherent(&hdr->pub_long_chunks), n_lc_max);
+    const uint32_t n_lc = min(cur.n_lc, n_lc_max);
     const uint32_t total = n_lc * (uint32_t)tiles;
-    cur.n_lc = n_lc;
-    cur.n_lr = (uint32_t)n_lr;
-    for (int r = tid; r < n_lr; r += kSortThreads) cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
-    __syncthreads();
 
     for (;;) {
         if (!cur.have_task) {   // uniform
@@ -687,6 +689,12 @@ __device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, Com
         }
         const uint32_t t = cur.task;
         if (t >= n_tasks) return false;   // uniform
+        if (!cur.runs_loaded) {   // uniform: this workgroup's first task
+            for (int r = tid; r < n_lr; r += kSortThreads)
+                cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
+            __syncthreads();
+            cur.runs_loaded = true;
+        }
         // the run: the last one whose first task is at or before t
         int lo = 0, hi = n_lr;
         while (hi - lo > 1) {
@@ -761,7 +769,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     float *__restrict__ partial, int64_t partial_stride, uint32_t epoch, int defer_odd_shares) {
     __shared__ AccSmem sm;
     __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
-    __shared__ uint32_t s_long[4];   // long-share hand-off (kLongElect ...)
+    __shared__ uint32_t s_long[kLongWords];   // long-share hand-off (kLongElect ...)
     const int tid = threadIdx.x;
     const uint32_t n_lc_max = (uint32_t)(2 * n / 11), n_lr_max = (uint32_t)(n / 11);
     const __amdgpu_buffer_rsrc_t units_rs = buffer_range(units, n_lc_max * (uint32_t)kUnitRecordBytes);
@@ -769,6 +777,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     if (tid == 0) {   // read after the barriers of either first phase
         s_long[kLongElect] = 0u;
         s_long[kLongState] = 0u;
+        s_long[kLongTasks] = 0u;
     }
 
     if (blockIdx.x == 0) {
@@ -795,7 +804,8 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     cur.have_task = false;
     cur.task = 0u;
     cur.spins = 0;
-    cur.n_lc = cur.n_lr = 0u;
+    cur.n_lc = cur.n_lr = cur.n_tasks = 0u;
+    cur.runs_loaded = false;
     for (;;) {
         for (; w < w_end; ++w) {
             ++call;
@@ -808,6 +818,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
                 flag_seen = (s_long[kLongState] & kStateNoFlag) == 0u;
                 cur.n_lc = s_long[kLongChunks];
                 cur.n_lr = s_long[kLongRuns];
+                cur.n_tasks = s_long[kLongTasks];
             }
             if (took && mark == 2u && tid == 0)
                 fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);

@@ -36,11 +36,12 @@ struct WsHeader {
     int32_t pad0[27];
     // line 1: published by the sorting workgroup, then `ready` is set to the
     // call's epoch (nonzero); the last workgroup to finish sets it back to 0
+    // (ready and the three counts form one 16-byte word, read by one load)
     uint32_t ready;
-    int32_t wait_timeouts;    // bounded waits that gave up (never expected)
+    uint32_t pub_tasks;       // combine tasks of this call
     uint32_t pub_long_chunks; // long chunks of this call
     uint32_t pub_long_runs;   // long runs of this call
-    uint32_t pub_tasks;       // combine tasks of this call
+    int32_t wait_timeouts;    // bounded waits that gave up (never expected)
     int32_t stolen_shares;    // long shares a waiting combine task took over in the last call
     int32_t pad1[26];
     // line 2: next combine task to hand out
