@@ -32,6 +32,37 @@ def test_header_functions_are_exported():
     assert set(names) == set(B.EXPORTS)
 
 
+def header_constants():
+    """Every `#define EWG_X <int>` and `EWG_X = <int>` enumerator of the header."""
+    out = {}
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if fn.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(HEADER_DIR, fn)).read(), flags=re.S)
+            out.update({k: int(v) for k, v in re.findall(r"^#define\s+(EWG_\w+)\s+(\d+)\s*$", text, flags=re.M)})
+            out.update({k: int(v) for k, v in re.findall(r"\b(EWG_\w+)\s*=\s*(\d+)", text)})
+    return out
+
+
+def test_binding_constants_match_the_header():
+    c = header_constants()
+    expected = {
+        "EWG_MIN_TOKENS": B.MIN_TOKENS, "EWG_MAX_TOKENS": B.MAX_TOKENS, "EWG_NROWS": B.NROWS,
+        "EWG_MANY_MAX_TOKENS": B.MANY_MAX_TOKENS, "EWG_MANY_MAX_EMBEDDINGS": B.MANY_MAX_EMBEDDINGS,
+        "EWG_WS_WAIT_TIMEOUTS_OFFSET": B.WS_WAIT_TIMEOUTS_OFFSET,
+        "EWG_WS_STOLEN_SHARES_OFFSET": B.WS_STOLEN_SHARES_OFFSET,
+        "EWG_INT32": B.EWG_INT32, "EWG_INT64": B.EWG_INT64, "EWG_BF16": B.EWG_BF16,
+        "EWG_FP32": B.EWG_FP32, "EWG_OK": B.EWG_OK, "EWG_UNSUPPORTED": B.EWG_UNSUPPORTED,
+        "EWG_INVALID_ARGUMENT": B.EWG_INVALID_ARGUMENT,
+        "EWG_WORKSPACE_TOO_SMALL": B.EWG_WORKSPACE_TOO_SMALL, "EWG_HIP_ERROR": B.EWG_HIP_ERROR,
+    }
+    assert set(expected) <= set(c), sorted(set(expected) - set(c))
+    for k, v in expected.items():
+        assert c[k] == v, f"{k}: header {c[k]}, binding {v}"
+    # the two diagnostic words lie in the workspace header, 4-byte aligned, apart
+    assert c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] % 4 == 0 and c["EWG_WS_STOLEN_SHARES_OFFSET"] % 4 == 0
+    assert c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] != c["EWG_WS_STOLEN_SHARES_OFFSET"]
+
+
 def test_position_bits():
     assert ewg.position_bits(1) == 0
     assert ewg.position_bits(2) == 1
