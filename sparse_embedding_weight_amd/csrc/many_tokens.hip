@@ -15,7 +15,8 @@
 //
 //   1. tile_sort_kernel (one workgroup per tile): keys (id << 13 | position
 //      in the tile) radix-sorted in LDS (sort_lds.h), written out sorted.
-//   2. rank_kernel (one workgroup per 1024 sorted keys of a tile): every
+//   2. rank_kernel (one workgroup per 256 sorted keys of a tile, four
+//      threads per key, each searching one of four tiles staged together): every
 //      position of tile t precedes every position of tile t + 1, so the
 //      global (id, position) rank of a key is its index in its own sorted
 //      tile plus, in every earlier tile, the keys with id <= its id and, in
@@ -46,7 +47,8 @@ namespace {
 constexpr int kTileBits = 13;              // positions inside a tile
 constexpr int kTileKeys = 1 << kTileBits;  // keys one workgroup sorts
 static_assert(kTileKeys == kMaxTokens, "a tile is one LDS sort");
-constexpr int kRankSlice = kSortThreads;   // sorted keys per rank_kernel workgroup
+constexpr int kRankGroup = 4;              // tiles staged and searched at once by rank_kernel
+constexpr int kRankSlice = kSortThreads / kRankGroup;   // sorted keys per rank_kernel workgroup
 constexpr int kListItems = 2;              // ranks per thread of chunk_list_kernel
 constexpr int kListBlock = kSortThreads * kListItems;   // ranks per chunk_list_kernel workgroup
 constexpr int kSumThreads = 256;           // chunk_sums_kernel workgroup
@@ -116,70 +118,87 @@ __global__ __launch_bounds__(kSortThreads) void rank_kernel(int n, int tiles, in
                                                             uint32_t *__restrict__ gid,
                                                             uint32_t *__restrict__ cw,
                                                             uint32_t *__restrict__ glen) {
-    __shared__ uint32_t s_tile[2][kTileKeys];   // the tile being searched, the next one arriving
+    __shared__ uint32_t s_tile[kRankGroup][kTileKeys];         // a group of tiles, all searched at once
+    __shared__ uint32_t s_part[kRankGroup][3][kRankSlice];     // per tile lane: before, start, length
     __shared__ uint32_t s_res[3][kRankSlice];   // per id of the slice: before, run start, run length
     __shared__ uint64_t s_scan[kSortWaves + 1];
     int32_t bad;
     if (any_bad(hdr, tiles, &bad)) return;   // uniform: nothing is accumulated
     const int tid = threadIdx.x;
+    // thread = (key of the slice kl, tile lane ts): the kRankGroup threads of
+    // a key search one tile each of every group of tiles
+    const int kl = tid % kRankSlice, ts = tid / kRankSlice;
     const int t = blockIdx.x / (kTileKeys / kRankSlice);
-    const int i = (blockIdx.x % (kTileKeys / kRankSlice)) * kRankSlice + tid;   // index in the sorted tile
+    const int i = (blockIdx.x % (kTileKeys / kRankSlice)) * kRankSlice + kl;   // index in the sorted tile
     const int nt = n - t * kTileKeys < kTileKeys ? n - t * kTileKeys : kTileKeys;
     const bool valid = i < nt;
     const uint32_t key = valid ? tkeys[t * kTileKeys + i] : 0xffffffffu;
     const uint32_t x = key >> kTileBits;
-    const bool head = valid && (tid == 0 || (tkeys[t * kTileKeys + i - 1] >> kTileBits) != x);
+    const bool head = valid && (kl == 0 || (tkeys[t * kTileKeys + i - 1] >> kTileBits) != x);
     uint64_t heads;
-    const uint32_t excl = (uint32_t)block_exclusive_scan(head ? 1u : 0u, s_scan, &heads);
-    const uint32_t ord = head ? excl : excl - 1u;   // the slice's id groups in order
+    const uint32_t excl =
+        (uint32_t)block_exclusive_scan(head && ts == 0 ? 1u : 0u, s_scan, &heads);
+    const uint32_t ord = head ? excl : excl - 1u;   // for ts == 0: the slice's id groups in order
 
-    // Every tile in turn, staged in LDS (thread j moves keys [8j, 8j + 8));
-    // the loads of the next two tiles are in flight while one is searched.
-    // Each id group of the slice counts, in every tile k, the keys below x and
-    // below x + 1 (ids < x, ids <= x).
+    // Each id group of the slice counts, in every tile k, the keys below x
+    // and below x + 1 (ids < x, ids <= x): tiles are staged kRankGroup at a
+    // time (thread j moves keys [8j, 8j + 8) of each), and the group's head
+    // key is searched in tile k by its thread of lane k % kRankGroup.
     const uint32_t key_a = x << kTileBits, key_b = (x + 1u) << kTileBits;
     uint32_t before = 0u, start = 0u, len = 0u;
-    auto fetch = [&](int k, uint4 (&r)[2]) {
-        const int nk = n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys;
-        const uint4 *src = reinterpret_cast<const uint4 *>(tkeys + (size_t)k * kTileKeys);
+    for (int g0 = 0; g0 < tiles; g0 += kRankGroup) {
+        uint4 r[kRankGroup][2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int e = tid * kSortItems + 4 * q;   // first key of this piece
-            r[q] = e < nk ? src[e / 4] : uint4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        for (int q = 0; q < kRankGroup; ++q) {
+            const int k = g0 + q;
+            const int nk = k < tiles ? (n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys) : 0;
+            const uint4 *src = reinterpret_cast<const uint4 *>(tkeys + (size_t)k * kTileKeys);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = tid * kSortItems + 4 * h;   // first key of this piece
+                r[q][h] = e < nk ? src[e / 4]
+                                 : uint4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+            }
         }
-    };
-    // tile k: into LDS buffer k & 1 (last searched two tiles ago), then the
-    // registers refill with tile k + 2
-    auto step = [&](int k, uint4 (&r)[2]) {
-        uint4 *dst = reinterpret_cast<uint4 *>(s_tile[k & 1]);
-        dst[2 * tid] = r[0];
-        dst[2 * tid + 1] = r[1];
+        if (g0 > 0) __syncthreads();   // the previous group's searches are done
+#pragma unroll
+        for (int q = 0; q < kRankGroup; ++q) {
+            uint4 *dst = reinterpret_cast<uint4 *>(s_tile[q]);
+            dst[2 * tid] = r[q][0];
+            dst[2 * tid + 1] = r[q][1];
+        }
         __syncthreads();
-        if (k + 2 < tiles) fetch(k + 2, r);
-        if (head) {
+        const int k = g0 + ts;
+        if (head && k < tiles) {
             const uint32_t nk = (uint32_t)(n - k * kTileKeys < kTileKeys ? n - k * kTileKeys : kTileKeys);
-            const uint32_t lo = lds_count_below(s_tile[k & 1], nk, key_a);
-            const uint32_t hi = lds_count_below(s_tile[k & 1], nk, key_b);
+            const uint32_t lo = lds_count_below(s_tile[ts], nk, key_a);
+            const uint32_t hi = lds_count_below(s_tile[ts], nk, key_b);
             start += lo;
             len += hi - lo;
             if (k < t) before += hi;       // earlier positions of this id and smaller ids
             else if (k > t) before += lo;  // smaller ids only
         }
-    };
-    uint4 ra[2], rb[2];
-    fetch(0, ra);
-    if (tiles > 1) fetch(1, rb);
-    for (int k = 0; k < tiles; k += 2) {
-        step(k, ra);
-        if (k + 1 < tiles) step(k + 1, rb);   // uniform
     }
     if (head) {
+        s_part[ts][0][kl] = before;
+        s_part[ts][1][kl] = start;
+        s_part[ts][2][kl] = len;
+    }
+    __syncthreads();
+    if (head && ts == 0) {   // the key's lane 0 adds up its lanes' counts
+        before = start = len = 0u;
+#pragma unroll
+        for (int q = 0; q < kRankGroup; ++q) {
+            before += s_part[q][0][kl];
+            start += s_part[q][1][kl];
+            len += s_part[q][2][kl];
+        }
         s_res[0][ord] = before;
         s_res[1][ord] = start;
         s_res[2][ord] = len;
     }
     __syncthreads();
-    if (!valid) return;
+    if (ts != 0 || !valid) return;   // the rest is per key, in lane 0
     const uint32_t rank = s_res[0][ord] + (uint32_t)i;
     const uint32_t run0 = s_res[1][ord], rlen = s_res[2][ord];
     if (rank >= (uint32_t)n) return;   // never: the ranks of the n keys are 0 .. n-1
