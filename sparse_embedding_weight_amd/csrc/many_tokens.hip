@@ -386,26 +386,40 @@ __global__ __launch_bounds__(kSortThreads) void combine_kernel(
     const float *__restrict__ partial, int64_t partial_stride, typename M::T *__restrict__ main_grad,
     int64_t mg_stride, uint32_t max_long_chunks, uint32_t max_long_runs, int hidden) {
     __shared__ float stage[kManyStage];
+    __shared__ uint32_t s_run;
     const uint32_t n_tasks = hdr->n_tasks;
     const int n_lr = (int)min(hdr->n_long_runs, max_long_runs);
     for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
-        // the run: the last one whose first task is at or before t
-        int lo = 0, hi = n_lr;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (runs[mid].w <= t) lo = mid; else hi = mid;
+        // the run: the last one whose first task is at or before t (first
+        // tasks never decrease). The first wave probes 64 records at once,
+        // narrowing the range 64-fold per round trip.
+        if (threadIdx.x < 64) {
+            const uint32_t lane = threadIdx.x;
+            uint32_t lo = 0u, hi = n_lr > 0 ? (uint32_t)n_lr : 1u;
+            while (hi - lo > 1u) {
+                const uint32_t step = (hi - lo + 63u) / 64u;
+                const uint32_t idx = lo + lane * step;
+                const uint32_t v = idx < hi ? runs[idx].w : 0xffffffffu;
+                const uint64_t m = __ballot(v <= t);   // lanes 0 .. k: a prefix
+                const uint32_t k = m ? 63u - (uint32_t)__clzll((long long)m) : 0u;
+                lo += k * step;
+                hi = min(hi, lo + step);
+            }
+            if (lane == 0) s_run = lo;
         }
-        const u32x4 rec = runs[lo];
+        __syncthreads();
+        const u32x4 rec = runs[s_run];
         const uint32_t row = rec.x, first = rec.y, chunks = rec.z;
         const int wdt = combine_width<kManyStage>((int)chunks, hidden);
         const int64_t col0 = (int64_t)(t - rec.w) * wdt;
         // a record that does not describe this call's work (never expected) is skipped
-        if (n_lr < 1 || rec.w > t || row >= (uint32_t)num_embeddings || chunks < 1 ||
-            first >= max_long_chunks || chunks > max_long_chunks - first || col0 >= hidden)
-            continue;
-        combine_block<G, M, kManyStage>(stage, row, first, chunks, col0, wdt, partial, partial_stride,
-                            main_grad, mg_stride, hidden);
-        __syncthreads();
+        const bool valid = n_lr >= 1 && rec.w <= t && row < (uint32_t)num_embeddings &&
+                           chunks >= 1 && first < max_long_chunks &&
+                           chunks <= max_long_chunks - first && col0 < hidden;
+        if (valid)   // uniform
+            combine_block<G, M, kManyStage>(stage, row, first, chunks, col0, wdt, partial,
+                                            partial_stride, main_grad, mg_stride, hidden);
+        __syncthreads();   // stage and s_run are free for the next task
     }
 }
 
