@@ -40,7 +40,7 @@ __device__ __forceinline__ int combine_width(int chunks, int hidden) {
 // straight-line code, so they are all in flight before the first add.
 // dest < 0: finish into main_grad row `row`; else store the fp32 chunk sums
 // in row `dest` of the partial buffer.
-template <typename G, typename M, int VEC, int R, int NT>
+template <typename G, typename M, int VEC, int R, int NT, int CP>
 __device__ __forceinline__ void chunk_tiles(const int32_t *pos, int row, int dest,
                                             const typename G::T *__restrict__ grad,
                                             int64_t grad_stride, typename M::T *__restrict__ main_grad,
@@ -96,20 +96,21 @@ __device__ __forceinline__ void chunk_tiles(const int32_t *pos, int row, int des
             for (int s = 0; s < S; ++s) store_piece<MT, P>(mrow + col[k][s], &out[s * P]);
         }
     } else {
-        // read by another workgroup in this launch: device-coherent stores
+        // CP: device-coherent stores when another workgroup of this launch
+        // reads them, plain ones when only a later kernel does
         const __amdgpu_buffer_rsrc_t prow =
             buffer_range(partial + (int64_t)dest * partial_stride, (uint32_t)(partial_stride * 4));
 #pragma unroll
         for (int k = 0; k < NT; ++k)
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                store_coherent_floats<P>(prow, (uint32_t)col[k][s] * 4u, &acc[k][s * P]);
+                store_coherent_floats<P, CP>(prow, (uint32_t)col[k][s] * 4u, &acc[k][s * P]);
     }
 }
 
 // The ragged last tile (starting at column tile_col) of one chunk, element by
 // element, in the same lane layout.
-template <typename G, typename M, int VEC>
+template <typename G, typename M, int VEC, int CP>
 __device__ __forceinline__ void chunk_ragged_tile(const int32_t *pos, int nrows, int row, int dest,
                                                   const typename G::T *__restrict__ grad,
                                                   int64_t grad_stride,
@@ -129,8 +130,9 @@ __device__ __forceinline__ void chunk_ragged_tile(const int32_t *pos, int nrows,
                 MT *m = main_grad + (int64_t)row * mg_stride + j;
                 *m = finish<G, M>(0.0f + acc, *m);
             } else {
-                store_coherent(reinterpret_cast<uint32_t *>(partial + (int64_t)dest * partial_stride + j),
-                               __float_as_uint(acc));
+                float *d = partial + (int64_t)dest * partial_stride + j;
+                if constexpr (CP != 0) store_coherent(reinterpret_cast<uint32_t *>(d), __float_as_uint(acc));
+                else *d = acc;
             }
         }
 }
@@ -148,7 +150,7 @@ constexpr int tiles_per_batch() {
 
 // Tiles [t0, t_end) of one chunk of R rows: full tiles in batches of loads,
 // then the ragged last tile if it is among them.
-template <typename G, typename M, int VEC, int R>
+template <typename G, typename M, int VEC, int R, int CP>
 __device__ __forceinline__ void chunk_tile_range(const int32_t *pos, int row, int dest,
                                                  const typename G::T *__restrict__ grad,
                                                  int64_t grad_stride,
@@ -160,18 +162,18 @@ __device__ __forceinline__ void chunk_tile_range(const int32_t *pos, int row, in
     const int t_full = t_end < full_tiles ? t_end : full_tiles;
     int t = t0;
     for (; t + B <= t_full; t += B)
-        chunk_tiles<G, M, VEC, R, B>(pos, row, dest, grad, grad_stride, main_grad, mg_stride,
+        chunk_tiles<G, M, VEC, R, B, CP>(pos, row, dest, grad, grad_stride, main_grad, mg_stride,
                                      partial, partial_stride, t * 64 * VEC);
     for (; t < t_full; ++t)
-        chunk_tiles<G, M, VEC, R, 1>(pos, row, dest, grad, grad_stride, main_grad, mg_stride,
+        chunk_tiles<G, M, VEC, R, 1, CP>(pos, row, dest, grad, grad_stride, main_grad, mg_stride,
                                      partial, partial_stride, t * 64 * VEC);
     if (t < t_end)
-        chunk_ragged_tile<G, M, VEC>(pos, R, row, dest, grad, grad_stride, main_grad, mg_stride,
+        chunk_ragged_tile<G, M, VEC, CP>(pos, R, row, dest, grad, grad_stride, main_grad, mg_stride,
                                      partial, partial_stride, hidden, t * 64 * VEC);
 }
 
 // Dispatch on the row count of a chunk (1..10).
-template <typename G, typename M, int VEC>
+template <typename G, typename M, int VEC, int CP = kDeviceScope>
 __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, int row, int dest,
                                                 const typename G::T *__restrict__ grad,
                                                 int64_t grad_stride,
@@ -181,7 +183,7 @@ __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, i
                                                 int t_end, int full_tiles) {
 #define EWG_CHUNK(R)                                                                           \
     case R:                                                                                    \
-        chunk_tile_range<G, M, VEC, R>(pos, row, dest, grad, grad_stride, main_grad, mg_stride, \
+        chunk_tile_range<G, M, VEC, R, CP>(pos, row, dest, grad, grad_stride, main_grad, mg_stride, \
                                        partial, partial_stride, hidden, t0, t_end, full_tiles); \
         break;
     switch (nrows) {
@@ -199,7 +201,7 @@ __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, i
 // as many at a time as fit, and every column's running total adds them in
 // chunk order starting from +0; the total is then rounded once and added to
 // main_grad row `row`. wdt is combine_width<STAGE>(chunks, hidden).
-template <typename G, typename M, int STAGE = kStageFloats>
+template <typename G, typename M, int STAGE = kStageFloats, int CP = kDeviceScope>
 __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32_t first,
                                               uint32_t chunks, int64_t col0, int wdt,
                                               const float *__restrict__ partial,
@@ -238,7 +240,7 @@ __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32
             const int kk = p / quads, q = p - kk * quads;
             const uint32_t off = p < pieces ? (uint32_t)(((int64_t)kk * partial_stride + 4 * q) * 4)
                                             : 0xfffffff0u;
-            v[i] = load_coherent16(rs, off);
+            v[i] = load_coherent16<CP>(rs, off);
         }
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {

@@ -138,8 +138,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void *base,
                                              kRawBufferWord3);
 }
 
+template <int CP = kDeviceScope>
 __device__ __forceinline__ u32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kDeviceScope);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, CP);
 }
 
 __device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
@@ -148,8 +149,8 @@ __device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint3
 }
 
 // P consecutive floats (P = 1, 2 or a multiple of 4), aligned to
-// min(16, 4 * P) bytes.
-template <int P>
+// min(16, 4 * P) bytes; CP = 0 for data read only by a later kernel.
+template <int P, int CP = kDeviceScope>
 __device__ __forceinline__ void store_coherent_floats(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
                                                       const float *v) {
     if constexpr (P % 4 == 0) {
@@ -157,15 +158,14 @@ __device__ __forceinline__ void store_coherent_floats(__amdgpu_buffer_rsrc_t r, 
         for (int k = 0; k < P / 4; ++k) {
             const u32x4 w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
                              __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
-            __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(byte_off + 16u * k), 0, kDeviceScope);
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(byte_off + 16u * k), 0, CP);
         }
     } else if constexpr (P == 2) {
         const u32x2 w = {__float_as_uint(v[0]), __float_as_uint(v[1])};
-        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)byte_off, 0, kDeviceScope);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)byte_off, 0, CP);
     } else {
         static_assert(P == 1, "pieces of 1, 2 or 4k floats");
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, (int)byte_off, 0,
-                                              kDeviceScope);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, (int)byte_off, 0, CP);
     }
 }
 

@@ -372,7 +372,8 @@ __global__ __launch_bounds__(kSumThreads) void chunk_sums_kernel(
         }
         const int t0 = (int)g * kSumTilesPerUnit;
         const int t_end = t0 + kSumTilesPerUnit < tiles ? t0 + kSumTilesPerUnit : tiles;
-        chunk_tiles_any<G, M, VEC>(pos, rows, (int)row, dest == 0xffffffffu ? -1 : (int)dest,
+        // plain stores: only the combine kernel, launched after this one, reads the sums
+        chunk_tiles_any<G, M, VEC, 0>(pos, rows, (int)row, dest == 0xffffffffu ? -1 : (int)dest,
                                    grad, grad_stride, main_grad, mg_stride, partial,
                                    partial_stride, hidden, t0, t_end, full_tiles);
     }
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(kSortThreads) void combine_kernel(
                            chunks >= 1 && first < max_long_chunks &&
                            chunks <= max_long_chunks - first && col0 < hidden;
         if (valid)   // uniform
-            combine_block<G, M, kManyStage>(stage, row, first, chunks, col0, wdt, partial,
+            combine_block<G, M, kManyStage, 0>(stage, row, first, chunks, col0, wdt, partial,
                                             partial_stride, main_grad, mg_stride, hidden);
         __syncthreads();   // stage and s_run are free for the next task
     }
