@@ -347,6 +347,41 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 
 // ---- phase 1: the sorting workgroup -------------------------------------------
 
+constexpr int kQuickCheckKeys = kMaxTokens / 4;   // kept positions the quick check takes
+
+// True if some id occurs on more than kNRows of the kept keys (at most
+// kQuickCheckKeys, left-out and missing positions hold all ones): a count
+// table of the kept ids with linear probing over kMaxTokens / 2 (id + 1,
+// count) pairs in the sort's second key buffer, at most half full. Every
+// thread must call it; it returns the same value in every thread.
+__device__ __forceinline__ bool kept_id_exceeds_rows(SortSmem &ss, int pos_bits) {
+    constexpr int kSlots = kMaxTokens / 2;
+    static_assert(2 * kQuickCheckKeys <= kSlots, "the table stays at most half full");
+    const int tid = threadIdx.x;
+    uint32_t *tab = ss.keys[1];
+    for (int i = tid; i < 2 * kSlots; i += kSortThreads) tab[i] = 0u;
+    if (tid == 0) ss.long_seen = 0;
+    __syncthreads();
+    int seen = 0;
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const uint32_t key = ss.keys[0][i * kSortThreads + tid];
+        if (key == 0xffffffffu) continue;
+        const uint32_t k1 = (key >> pos_bits) + 1u;
+        uint32_t h = (k1 * 0x9E3779B1u) >> (32 - 12);
+        static_assert(kSlots == 1 << 12, "12-bit slot numbers");
+        for (;;) {
+            const uint32_t old = atomicCAS(&tab[2 * h], 0u, k1);
+            if (old == 0u || old == k1) break;
+            h = (h + 1u) & (kSlots - 1);
+        }
+        if (atomicAdd(&tab[2 * h + 1], 1u) >= (uint32_t)kNRows) seen = 1;
+    }
+    if (seen) atomicOr(&ss.long_seen, 1);
+    __syncthreads();
+    return ss.long_seen != 0;
+}
+
 // Sort, mark runs, write the unit and run records, zero the runs' unit counts
 // and the tickets, publish the counts and raise the flag. With an id out of
 // range there is nothing to do: all counts are 0.
@@ -364,8 +399,17 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
     const SortOutputs out0 = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
                               nullptr, nullptr};
     const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits, id_base, skip_outside);
+    // A vocabulary shard that keeps few positions often has no id on more than
+    // 10 of them, and then no long run: the flag goes up without the sort.
+    const bool few = !bad && ss.n_keys <= kQuickCheckKeys;   // uniform
     if (bad) {
         report_invalid(out0, bad);
+    } else if (few && !kept_id_exceeds_rows(ss, pos_bits)) {
+        if (tid == 0) {
+            hdr->invalid_ids = 0;
+            hdr->num_long_runs = 0;
+            hdr->num_long_chunks = 0;
+        }
     } else {
         const int cur = radix_sort_ids(ss, pos_bits, id_bits);
         // after the sort, aux holds: the run of every long chunk, the long-run

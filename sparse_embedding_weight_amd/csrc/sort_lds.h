@@ -41,6 +41,7 @@ struct SortSmem {
     int bad;
     int n_keys;                                 // keys of ids inside the table (sorted first)
     int n_chunks, n_long, n_long_chunks, n_runs;
+    int long_seen;                              // a quick check found an id on > 10 keys
 };
 
 // Sort results for one call.

@@ -328,6 +328,33 @@ def test_vocab_shard_edges():
     assert torch.equal(_bits(mg2), _bits(mg))
 
 
+def test_vocab_shard_quick_check_boundary():
+    """A shard call that keeps at most 2048 positions checks whether any id has more
+    than 10 of them and skips the sort when none has: ids on exactly 10 and 11
+    positions, and hot ids on 2000 and on 2049 positions, in single-row shards and
+    inside wider ones, all equal to the oracle."""
+    rng = np.random.default_rng(73)
+    n, hidden, v = 6000, 72, 1 << 15
+    ids_np = rng.integers(1000, v, size=n)
+    perm = rng.permutation(n)
+    ids_np[perm[:10]] = 100            # 10 rows: one chunk, no long run
+    ids_np[perm[10:21]] = 200          # 11 rows: the smallest long run
+    ids_np[perm[21:2021]] = 300        # 2000 kept positions: checked, long
+    ids_np[perm[2021:4070]] = 400      # 2049 kept positions: above the check, sorted
+    print("[shard quick check] n=6000 hidden=72", flush=True)
+    ids_t = torch.from_numpy(ids_np).to(torch.int32).cuda()
+    grad = wl.normal_tensor(rng, (n, hidden), 0.01, "bf16").cuda()
+    mg = wl.normal_tensor(rng, (v, hidden), 1e-3, "fp32").cuda()
+    before = mg.clone()
+    ws = ewg.new_workspace(n, hidden, "cuda")
+    _shard_calls(ids_t, grad, mg, [0, 100, 101, 200, 201, 300, 301, 400, 401, 1000, v], ws=ws)
+    assert ewg.wait_timeouts(ws) == 0
+    _check_against_oracle(ids_t, grad, before, mg)
+    mg2 = before.clone()
+    _shard_calls(ids_t, grad, mg2, [0, 150, 250, 350, 1000, v], ws=ws)
+    assert torch.equal(_bits(mg2), _bits(mg))
+
+
 # ---- launch sizes: few workgroups (long shares, many rounds) and more than fit at once ----
 
 @pytest.mark.parametrize("grid", ["2", "3", "16", "2x", "3x"])
