@@ -68,14 +68,13 @@ constexpr uint64_t kStealAfterTicks = 20000;   // 200 us of the 100 MHz clock: a
 constexpr int kHashSlots = 16384;        // > 2 x kMaxTokens: linear probing always ends
 constexpr int kHashBits = 14;
 constexpr int kOwnedMax = 256;           // short runs gathered per round by one follower
-constexpr uint32_t kIdMask = (1u << 20) - 1;   // key word: id + 1 in 20 bits, round mark above
 constexpr uint32_t kNoSlot = 0xffffu;    // slot of a position whose id is left out
 constexpr int kMaxLongRuns = kMaxTokens / 11;
 constexpr int kMaxLongChunks = 2 * kMaxTokens / 11;
 
 struct FollowerSmem {
-    uint32_t key[kHashSlots];               // (id + 1) | (round-local run + 1) << 20; 0 = empty
-    uint32_t cnt[kHashSlots];               // occurrences | first position << 16
+    uint32_t key[kHashSlots];               // (id + 1) | first position << (32 - position bits); 0 = empty
+    uint32_t cnt[kHashSlots];               // occurrences (saturating at 11) | (round-local run + 1) << 16
     uint16_t slot_of_pos[kMaxTokens];
     uint16_t run_pos[kOwnedMax][kNRows];
     uint32_t run_len[kOwnedMax];
@@ -119,7 +118,11 @@ __device__ __forceinline__ uint32_t hash_home(uint32_t id) {
 
 // Follower part 1: the runs of at most 10 rows in this follower's share.
 // Every follower inserts all ids into its LDS hash table (occurrences and the
-// first position per id, the slot of every position). Walking the positions
+// first position per id, the slot of every position). The first position
+// shares the key word with the id: id + 1 fills the low 32 - pos_bits bits
+// (the 31-bit key packing bounds id + 1 by 2^(31 - pos_bits)), the position
+// the bits above, so that an atomic minimum over the words of one id keeps
+// its smallest position. Walking the positions
 // in order, the first occurrence of every id with at most 10 occurrences
 // carries the byte cost of its run; follower `me` takes the runs whose cost
 // prefix starts in [me, me + 1) * total / followers. That order and those
@@ -129,7 +132,7 @@ __device__ __forceinline__ uint32_t hash_home(uint32_t id) {
 template <typename IdT, typename G, typename M, int VEC>
 __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT *__restrict__ ids,
                                                     int n, int num_embeddings, int64_t id_base,
-                                                    bool skip_outside,
+                                                    bool skip_outside, int pos_bits,
                                                     const typename G::T *__restrict__ grad,
                                                     int64_t grad_stride,
                                                     typename M::T *__restrict__ main_grad,
@@ -137,6 +140,8 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
                                                     int me, int followers) {
     const int tid = threadIdx.x;
     constexpr int kSlotsPerThread = kHashSlots / kSortThreads;
+    const int id_shift = 32 - pos_bits;
+    const uint32_t id_mask = (1u << id_shift) - 1u;
 
     // load the ids (all 8 loads in flight) while the table is cleared
     int64_t id[kSortItems];
@@ -156,11 +161,9 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
     // insert: occurrences per id, slot per position (kNoSlot for a position
     // whose id is left out)
     int bad = 0;
-    uint32_t slot[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int p = i * kSortThreads + tid;
-        slot[i] = kNoSlot;
         if (p >= n) continue;
         const int64_t v = id[i] - id_base;
         if (v < 0 || v >= num_embeddings) {
@@ -169,13 +172,17 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             continue;
         }
         const uint32_t k1 = (uint32_t)v + 1u;
+        const uint32_t kp = k1 | ((uint32_t)p << id_shift);
         uint32_t h = hash_home((uint32_t)v);
         for (;;) {
-            const uint32_t cur = fs.key[h];
-            if (cur == k1) break;
+            uint32_t cur = fs.key[h];
             if (cur == 0u) {
-                const uint32_t old = atomicCAS(&fs.key[h], 0u, k1);
-                if (old == 0u || old == k1) break;
+                cur = atomicCAS(&fs.key[h], 0u, kp);
+                if (cur == 0u) break;   // a new id, with this first position
+            }
+            if ((cur & id_mask) == k1) {   // the id is here: keep the smaller position
+                if ((cur >> id_shift) > (uint32_t)p) atomicMin(&fs.key[h], kp);
+                break;
             }
             h = (h + 1u) & (kHashSlots - 1);
         }
@@ -183,31 +190,10 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         // a frequent id stops taking atomics on its slot once it is known to be long
         if (fs.cnt[h] <= (uint32_t)kNRows) atomicAdd(&fs.cnt[h], 1u);
         fs.slot_of_pos[p] = (uint16_t)h;
-        slot[i] = h;
     }
     if (bad) atomicAdd(&fs.bad, bad);
     __syncthreads();
     if (fs.bad) return;   // uniform: the sorting workgroup reports it, nothing is touched
-
-    // first position of every id of at most kNRows rows: the high half starts
-    // at all ones, then the smallest position wins (the low half, the count,
-    // is the same for all)
-#pragma unroll
-    for (int k = 0; k < kSlotsPerThread; ++k) {
-        const int h = k * kSortThreads + tid;
-        if (fs.key[h]) fs.cnt[h] |= 0xffff0000u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
-        const int p = i * kSortThreads + tid;
-        if (p < n && slot[i] != kNoSlot) {
-            const uint32_t w = fs.cnt[slot[i]];
-            if ((w & 0xffffu) <= (uint32_t)kNRows && (w >> 16) > (uint32_t)p)
-                atomicMin(&fs.cnt[slot[i]], ((uint32_t)p << 16) | (w & 0xffffu));
-        }
-    }
-    __syncthreads();
 
     // per-tile byte cost of a run of c rows, in 16-byte lane loads
     const uint32_t row_cost = (uint32_t)(VEC * sizeof(typename G::T) + 15) / 16;
@@ -232,9 +218,8 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             v[j] = 0;
             const uint32_t h = p < n ? fs.slot_of_pos[p] : kNoSlot;
             if (h != kNoSlot) {
-                const uint32_t w = fs.cnt[h];
-                const uint32_t c = w & 0xffffu;
-                if ((w >> 16) == (uint32_t)p && c <= (uint32_t)kNRows)
+                const uint32_t c = fs.cnt[h] & 0xffffu;
+                if ((fs.key[h] >> id_shift) == (uint32_t)p && c <= (uint32_t)kNRows)
                     v[j] = (uint64_t)(c * row_cost + end_cost) | (1ull << 32);
             }
             sum += v[j];
@@ -272,10 +257,10 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
                     const int li = (int)((uint32_t)(x >> 32) - first) - r0;
                     if (li >= 0 && li < kOwnedMax) {
                         const uint32_t h = fs.slot_of_pos[p0 + j];
-                        fs.run_id[li] = (fs.key[h] & kIdMask) - 1u;
+                        fs.run_id[li] = (fs.key[h] & id_mask) - 1u;
                         fs.run_len[li] = 0u;
                         fs.run_slot[li] = h;
-                        fs.key[h] |= (uint32_t)(li + 1) << 20;
+                        fs.cnt[h] |= (uint32_t)(li + 1) << 16;
                     }
                 }
                 x += v[j];
@@ -291,7 +276,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         for (int i = 0; i < kSortItems; ++i) {
             const int p = i * kSortThreads + tid;
             if (p >= n || fs.slot_of_pos[p] == kNoSlot) continue;
-            const uint32_t m = fs.key[fs.slot_of_pos[p]] >> 20;
+            const uint32_t m = fs.cnt[fs.slot_of_pos[p]] >> 16;
             if (m) {
                 const uint32_t k = atomicAdd(&fs.run_len[m - 1u], 1u);
                 fs.run_pos[m - 1u][k] = (uint16_t)p;
@@ -339,7 +324,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         // after the last round every wave goes on by itself
         if (last_round) break;
         __syncthreads();
-        if (tid < n_round) fs.key[fs.run_slot[tid]] &= kIdMask;
+        if (tid < n_round) fs.cnt[fs.run_slot[tid]] &= 0xffffu;
         __syncthreads();
     }
 }
@@ -831,7 +816,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     } else {
         // the waves leave this one by one, as their short-run units run out
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
-                                            skip_outside != 0, grad, grad_stride,
+                                            skip_outside != 0, pos_bits, grad, grad_stride,
                                             main_grad, mg_stride, hidden, tiles,
                                             (int)blockIdx.x - 1, (int)gridDim.x - 1);
     }
