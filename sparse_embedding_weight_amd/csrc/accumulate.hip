@@ -81,6 +81,7 @@ struct FollowerSmem {
     uint32_t run_id[kOwnedMax];
     uint32_t run_slot[kOwnedMax];
     uint64_t scan[kSortWaves + 1];
+    uint32_t scan32[kSortWaves + 1];
     int bad;
     uint32_t first_rank;   // number of this follower's first run
     uint32_t n_mine;       // runs in this follower's share
@@ -151,9 +152,9 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         id[i] = (int64_t)ids[p < n ? p : n - 1];
     }
 #pragma unroll
-    for (int k = 0; k < kSlotsPerThread; ++k) {
-        fs.key[k * kSortThreads + tid] = 0u;
-        fs.cnt[k * kSortThreads + tid] = 0u;
+    for (int k = 0; k < kSlotsPerThread / 4; ++k) {   // 16-byte stores
+        reinterpret_cast<u32x4 *>(fs.key)[k * kSortThreads + tid] = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4 *>(fs.cnt)[k * kSortThreads + tid] = u32x4{0u, 0u, 0u, 0u};
     }
     if (tid == 0) fs.bad = 0;
     __syncthreads();
@@ -195,9 +196,16 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
     __syncthreads();
     if (fs.bad) return;   // uniform: the sorting workgroup reports it, nothing is touched
 
-    // per-tile byte cost of a run of c rows, in 16-byte lane loads
-    const uint32_t row_cost = (uint32_t)(VEC * sizeof(typename G::T) + 15) / 16;
-    const uint32_t end_cost = 2u * (uint32_t)(VEC * sizeof(typename M::T) + 15) / 16;
+    // per-tile byte cost of a run of c rows, in 16-byte lane loads; an item's
+    // scanned word is its cost | 1 << kCostBits (one run), so that the scan
+    // sums costs below bit kCostBits and counts runs above
+    constexpr uint32_t row_cost = (uint32_t)(VEC * sizeof(typename G::T) + 15) / 16;
+    constexpr uint32_t end_cost = 2u * (uint32_t)(VEC * sizeof(typename M::T) + 15) / 16;
+    constexpr int kCostBits = 17;
+    constexpr uint32_t kCostMask = (1u << kCostBits) - 1u;
+    static_assert((uint64_t)kMaxTokens * (kNRows * row_cost + end_cost) <= kCostMask &&
+                      kMaxTokens < (1u << (32 - kCostBits)),
+                  "costs and run counts share one 32-bit word");
     const int full_tiles = hidden / (64 * VEC);
     const int groups = (tiles + kTilesPerUnit - 1) / kTilesPerUnit;
 
@@ -207,38 +215,41 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             fs.n_mine = 0u;
             fs.next_unit = 0u;
         }
-        // positions in blocked order: thread t owns [8t, 8t + 8); low 32 bits
-        // of the scanned value = cost, high 32 bits = number of runs
+        // positions in blocked order: thread t owns [8t, 8t + 8), whose slots
+        // it reads with one 16-byte load
         const int p0 = tid * kSortItems;
-        uint64_t v[kSortItems];
-        uint64_t sum = 0;
+        static_assert(kSortItems == 8, "eight 16-bit slots per thread");
+        const u32x4 sw = reinterpret_cast<const u32x4 *>(fs.slot_of_pos)[tid];
+        const uint32_t sw4[4] = {sw.x, sw.y, sw.z, sw.w};
+        uint32_t v[kSortItems];
+        uint32_t sum = 0;
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const int p = p0 + j;
             v[j] = 0;
-            const uint32_t h = p < n ? fs.slot_of_pos[p] : kNoSlot;
+            const uint32_t h = p < n ? (sw4[j >> 1] >> (16 * (j & 1))) & 0xffffu : kNoSlot;
             if (h != kNoSlot) {
                 const uint32_t c = fs.cnt[h] & 0xffffu;
                 if ((fs.key[h] >> id_shift) == (uint32_t)p && c <= (uint32_t)kNRows)
-                    v[j] = (uint64_t)(c * row_cost + end_cost) | (1ull << 32);
+                    v[j] = (c * row_cost + end_cost) | (1u << kCostBits);
             }
             sum += v[j];
         }
-        uint64_t total;
-        const uint64_t run = block_exclusive_scan(sum, fs.scan, &total);
-        const uint64_t cost_all = total & 0xffffffffull;
+        uint32_t total;
+        const uint32_t run = block_exclusive_scan32(sum, fs.scan32, &total);
+        const uint64_t cost_all = total & kCostMask;
         const uint64_t lo = cost_all * (uint64_t)me / (uint64_t)followers;
         const uint64_t hi = cost_all * (uint64_t)(me + 1) / (uint64_t)followers;
         // runs are numbered in position order; this follower's (cost start in
         // [lo, hi)) are a contiguous range of numbers
         {
-            uint64_t x = run;
+            uint32_t x = run;
             uint32_t mine = 0;
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j) {
-                const uint64_t start = x & 0xffffffffull;
+                const uint64_t start = x & kCostMask;
                 if (v[j] && start >= lo && start < hi) {
-                    atomicMin(&fs.first_rank, (uint32_t)(x >> 32));
+                    atomicMin(&fs.first_rank, x >> kCostBits);
                     ++mine;
                 }
                 x += v[j];
@@ -249,12 +260,12 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         const uint32_t first = fs.first_rank;
         const int total_mine = (int)fs.n_mine;
         {
-            uint64_t x = run;
+            uint32_t x = run;
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j) {
-                const uint64_t start = x & 0xffffffffull;
+                const uint64_t start = x & kCostMask;
                 if (v[j] && start >= lo && start < hi) {
-                    const int li = (int)((uint32_t)(x >> 32) - first) - r0;
+                    const int li = (int)((x >> kCostBits) - first) - r0;
                     if (li >= 0 && li < kOwnedMax) {
                         const uint32_t h = fs.slot_of_pos[p0 + j];
                         fs.run_id[li] = (fs.key[h] & id_mask) - 1u;

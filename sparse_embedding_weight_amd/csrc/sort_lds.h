@@ -92,6 +92,36 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t *s
     return excl;
 }
 
+// The same over 32-bit values (the scan uses s_tmp[0 .. kSortWaves]).
+__device__ __forceinline__ uint32_t block_exclusive_scan32(uint32_t v, uint32_t *s_tmp,
+                                                           uint32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_tmp[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t w = lane < kSortWaves ? s_tmp[lane] : 0u;
+        uint32_t wi = w;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(wi, d, 64);
+            if (lane >= d) wi += o;
+        }
+        if (lane < kSortWaves) s_tmp[lane] = wi - w;
+        if (lane == kSortWaves - 1) s_tmp[kSortWaves] = wi;
+    }
+    __syncthreads();
+    const uint32_t excl = s_tmp[wave] + inc - v;
+    *total = s_tmp[kSortWaves];
+    __syncthreads();
+    return excl;
+}
+
 // Load the ids and build the keys in position order: wave w holds slots
 // [w*512, w*512 + 512) as 8 groups of 64; slots past n hold 0xffffffff, which
 // every pass ranks last. The key of position s holds id - id_base, for ids in
