@@ -495,7 +495,7 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     int64_t spins = 0;
     for (;;) {
         const u32x4 v = load_coherent16(h, (uint32_t)offsetof(WsHeader, ready));
-        if (__builtin_amdgcn_readfirstlane(v.x) == epoch) {
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(v.x) == epoch) {
             *n_tasks = __builtin_amdgcn_readfirstlane(v.y);
             *n_lc = __builtin_amdgcn_readfirstlane(v.z);
             *n_lr = __builtin_amdgcn_readfirstlane(v.w);
@@ -576,7 +576,7 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint3
     // updates are whole-wave atomics in which only lane 0 changes anything
     const uint32_t one = lane == 0 ? 1u : 0u;
     const uint32_t prev = call - 1u;
-    const bool stager = __builtin_amdgcn_readfirstlane(
+    const bool stager = (uint32_t)__builtin_amdgcn_readfirstlane(
                             atomicCAS(&s_long[kLongElect], prev, lane == 0 ? call : prev)) == prev;
     if (stager) {
         bool ok = true;
@@ -652,7 +652,7 @@ __device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint3
         }
         const uint32_t run = w[5] >> 16;
         // a record of another call (never expected) is counted and its unit skipped
-        if (__builtin_amdgcn_readfirstlane(rb.w) == epoch && run < n_lr) {
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(rb.w) == epoch && run < n_lr) {
             chunk_tiles_any<G, M, VEC>(pos, rows, 0, (int)c, grad, grad_stride, nullptr, 0,
                                        partial, partial_stride, hidden, tile, tile + 1,
                                        full_tiles);
