@@ -229,6 +229,37 @@ __device__ __forceinline__ uint64_t head_counts(uint32_t w) {
 
 constexpr uint64_t kField = (1ull << 21) - 1;
 
+// Four 64-bit values per thread in one pass over the workgroup: the sums
+// of a and b over all threads, the exclusive prefixes of c and d in thread
+// order, and the sums of c and d. Every thread must call it.
+__device__ __forceinline__ void block_scan4(uint64_t a, uint64_t b, uint64_t c, uint64_t d,
+                                            uint64_t (*s)[kSortWaves + 1], uint64_t *sum_a,
+                                            uint64_t *sum_b, uint64_t *pre_c, uint64_t *pre_d,
+                                            uint64_t *sum_c, uint64_t *sum_d) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t v[4] = {a, b, c, d};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = wave_inclusive_scan(v[k], lane);
+    if (lane == 63) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k][wave] = v[k];
+    }
+    __syncthreads();
+    if (wave < 4) {   // wave k scans the wave totals of value k
+        const uint64_t t = lane < kSortWaves ? s[wave][lane] : 0;
+        const uint64_t ti = wave_inclusive_scan(t, lane);
+        if (lane < kSortWaves) s[wave][lane] = ti - t;
+        if (lane == kSortWaves - 1) s[wave][kSortWaves] = ti;
+    }
+    __syncthreads();
+    *sum_a = s[0][kSortWaves];
+    *sum_b = s[1][kSortWaves];
+    *pre_c = s[2][wave] + v[2] - c;
+    *pre_d = s[3][wave] + v[3] - d;
+    *sum_c = s[2][kSortWaves];
+    *sum_d = s[3][kSortWaves];
+}
+
 __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int tiles,
                                                                   uint32_t max_long_runs,
                                                                   uint32_t max_long_chunks,
@@ -238,7 +269,7 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
                                                                   const uint32_t *__restrict__ glen,
                                                                   u32x4 *__restrict__ chunks,
                                                                   u32x4 *__restrict__ runs) {
-    __shared__ uint64_t s_scan[kSortWaves + 1];
+    __shared__ uint64_t s_scan4[4][kSortWaves + 1];
     const int tid = threadIdx.x;
     int32_t bad;
     if (any_bad(hdr, tiles, &bad)) {   // uniform
@@ -249,6 +280,21 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
         return;
     }
     const int r0 = blockIdx.x * kListBlock;
+    // this block's ranks: thread j owns [r0 + 2j, r0 + 2j + 2); 8-byte loads
+    // of the thread's words of each array, issued first so that they are in
+    // flight with the prefix counts below (a piece past n reads workspace
+    // that follows the array: its words are masked)
+    static_assert(kListItems == 2, "8-byte loads of two ranks");
+    const int s0 = r0 + tid * kListItems;
+    uint32_t w[kListItems] = {0u, 0u}, ids8[kListItems] = {0u, 0u}, len8[kListItems] = {0u, 0u};
+    if (s0 < n) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(cw + s0);
+        const uint2 b = *reinterpret_cast<const uint2 *>(gid + s0);
+        const uint2 c = *reinterpret_cast<const uint2 *>(glen + s0);
+        w[0] = a.x; w[1] = a.y;
+        ids8[0] = b.x; ids8[1] = b.y;
+        len8[0] = c.x; len8[1] = c.y;
+    }
     // counts over the ranks of earlier blocks (each block recounts them: no
     // block waits for another); 16-byte loads, 4 per thread in flight
     // together (r0 is a multiple of 4)
@@ -270,37 +316,23 @@ __global__ __launch_bounds__(kSortThreads) void chunk_list_kernel(int n, int til
             }
         }
     }
-    uint64_t base, base_tasks;
-    block_exclusive_scan(pre, s_scan, &base);
-    block_exclusive_scan(pre_tasks, s_scan, &base_tasks);
-
-    // this block's ranks: thread j owns [r0 + 2j, r0 + 2j + 2); 8-byte loads
-    // of the thread's words of each array, all in flight together (a piece
-    // past n reads workspace that follows the array: its words are masked)
-    static_assert(kListItems == 2, "8-byte loads of two ranks");
-    const int s0 = r0 + tid * kListItems;
-    uint32_t w[kListItems] = {0u, 0u}, ids8[kListItems] = {0u, 0u}, len8[kListItems] = {0u, 0u};
-    uint64_t mine = 0, mine_tasks = 0;
-    if (s0 < n) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(cw + s0);
-        const uint2 b = *reinterpret_cast<const uint2 *>(gid + s0);
-        const uint2 c = *reinterpret_cast<const uint2 *>(glen + s0);
-        w[0] = a.x; w[1] = a.y;
-        ids8[0] = b.x; ids8[1] = b.y;
-        len8[0] = c.x; len8[1] = c.y;
-    }
 #pragma unroll
     for (int j = 0; j < kListItems; ++j) {
         if (s0 + j >= n) w[j] = ids8[j] = len8[j] = 0u;
     }
+    uint64_t mine = 0, mine_tasks = 0;
 #pragma unroll
     for (int j = 0; j < kListItems; ++j) {
         mine += head_counts(w[j]);
         if ((w[j] & kHeadLongRun) == kHeadLongRun) mine_tasks += w[j] >> kTasksShift;
     }
-    uint64_t all, all_tasks;
-    uint64_t idx = base + block_exclusive_scan(mine, s_scan, &all);
-    uint64_t task = base_tasks + block_exclusive_scan(mine_tasks, s_scan, &all_tasks);
+    // one pass: totals of the earlier blocks' counts, exclusive prefixes of
+    // this block's
+    uint64_t base, base_tasks, all, all_tasks, idx, task;
+    block_scan4(pre, pre_tasks, mine, mine_tasks, s_scan4, &base, &base_tasks, &idx, &task, &all,
+                &all_tasks);
+    idx += base;
+    task += base_tasks;
 #pragma unroll
     for (int j = 0; j < kListItems; ++j) {
         if (w[j] & kHeadChunk) {
