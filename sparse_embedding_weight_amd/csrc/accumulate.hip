@@ -703,15 +703,21 @@ __device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, Com
     CombineSmem &cs = sm.comb;
     const int tid = threadIdx.x;
     // The counts are those the flag's load returned (without the flag, which
-    // never fails to come, there is no task to take). A workgroup takes a
-    // ticket first and loads the run records only for its first task, so
-    // one that finds the tasks gone leaves after one round trip.
+    // never fails to come, there is no task to take). The run records are
+    // loaded once, before the first ticket (taking the ticket first and the
+    // records only with a task cost 2 us on small calls, no time on large).
     if (!flag_seen) return false;
     const int n_lr = (int)min(cur.n_lr, n_lr_max);
     const uint32_t n_tasks = cur.n_tasks;
     if (n_lr == 0 || n_tasks == 0) return false;   // uniform
     const uint32_t n_lc = min(cur.n_lc, n_lc_max);
     const uint32_t total = n_lc * (uint32_t)tiles;
+    if (!cur.runs_loaded) {   // uniform
+        for (int r = tid; r < n_lr; r += kSortThreads)
+            cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
+        __syncthreads();
+        cur.runs_loaded = true;
+    }
 
     for (;;) {
         if (!cur.have_task) {   // uniform
@@ -729,12 +735,6 @@ __device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, Com
         }
         const uint32_t t = cur.task;
         if (t >= n_tasks) return false;   // uniform
-        if (!cur.runs_loaded) {   // uniform: this workgroup's first task
-            for (int r = tid; r < n_lr; r += kSortThreads)
-                cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
-            __syncthreads();
-            cur.runs_loaded = true;
-        }
         // the run: the last one whose first task is at or before t
         int lo = 0, hi = n_lr;
         while (hi - lo > 1) {
