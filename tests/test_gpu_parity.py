@@ -357,6 +357,54 @@ def test_vocab_shard_quick_check_boundary():
 
 # ---- launch sizes: few workgroups (long shares, many rounds) and more than fit at once ----
 
+def test_timed_entry_point_matches_plain_calls():
+    """accumulate_embedding_wgrad_timed, with the kernel's own events (4 events)
+    and with plain dispatches (events 2 and 3 NULL), adds exactly what the plain
+    entry point adds, and the events it records bound the kernel's own."""
+    import ctypes
+    from sparse_embedding_weight_amd import _binding as B
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    w = wl.WORKLOADS["zipf1.1_4096_v32000_h4096"]
+    ids = torch.from_numpy(wl.make_ids(w)).cuda().reshape(-1)
+    grad = wl.make_grad(w).cuda().reshape(ids.numel(), w.hidden)
+    mg0 = wl.make_main_grad(w, "cuda")
+    ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
+    plain = mg0.clone()
+    ewg.accumulate_embedding_wgrad(ids, grad, plain, workspace=ws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(4):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs.append(h.value)
+    stream = torch.cuda.current_stream().cuda_stream
+    try:
+        for kernel_events in (True, False):
+            mg = mg0.clone()
+            slots = (ctypes.c_void_p * 4)(*(evs if kernel_events else evs[:2] + [None, None]))
+            st = B.lib.accumulate_embedding_wgrad_timed(
+                ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), ids.numel(), w.hidden, w.vocab,
+                grad.stride(0), mg.stride(0), B.DTYPE_CODE[ids.dtype], B.DTYPE_CODE[grad.dtype],
+                B.DTYPE_CODE[mg.dtype], ws.data_ptr(), ws.numel(), stream, slots)
+            assert st == 0
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(mg), _bits(plain)), f"kernel_events={kernel_events}"
+            call = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(call), evs[0], evs[1]) == 0
+            assert 0.0 < call.value < 1000.0
+            if kernel_events:
+                kern = ctypes.c_float()
+                assert hip.hipEventElapsedTime(ctypes.byref(kern), evs[2], evs[3]) == 0
+                assert 0.0 < kern.value <= call.value
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    assert ewg.wait_timeouts(ws) == 0
+
+
 @pytest.mark.parametrize("grid", ["2", "3", "16", "2x", "3x"])
 @pytest.mark.parametrize("name", ["zipf1.1_4096_v32000_h4096", "longrun_8192_v129280_h7168"])
 def test_launch_sizes(grid, name, monkeypatch):
