@@ -60,7 +60,7 @@ def _run(call, ids, grad, mg):
     assert_rows_match(ids, grad, mg, before, rows, before_rows)
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_random_one_kernel_path(case):
     rng = np.random.default_rng(1000 + case)
     n, vocab, hidden, gd, md, idt, ids, pg, pm = _draw_case(rng, ewg.MIN_TOKENS, ewg.MAX_TOKENS, 200000)
@@ -73,7 +73,7 @@ def test_random_one_kernel_path(case):
     _run(ewg.accumulate_embedding_wgrad, *_tensors(rng, n, vocab, hidden, gd, md, idt, ids, pg, pm))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(16))
 def test_random_many_token_path(case):
     rng = np.random.default_rng(2000 + case)
     n, vocab, hidden, gd, md, idt, ids, pg, pm = _draw_case(rng, ewg.MAX_TOKENS + 1, 40000,
