@@ -201,7 +201,7 @@ __device__ __forceinline__ void chunk_tiles_any(const int32_t *pos, int nrows, i
 // as many at a time as fit, and every column's running total adds them in
 // chunk order starting from +0; the total is then rounded once and added to
 // main_grad row `row`. wdt is combine_width<STAGE>(chunks, hidden).
-template <typename G, typename M, int STAGE = kStageFloats, int CP = kDeviceScope>
+template <typename G, typename M, int STAGE = kStageFloats, int CP = kDeviceScope, int FOLD = 8>
 __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32_t first,
                                               uint32_t chunks, int64_t col0, int wdt,
                                               const float *__restrict__ partial,
@@ -265,14 +265,14 @@ __device__ __forceinline__ void combine_block(float *stage, uint32_t row, uint32
                 const float *col = &stage[j < wc ? j : wave_j0];
                 float acc = total[i];
                 // the adds stay in chunk order; the LDS reads of a group
-                // of 8 are all issued before the first add
+                // of FOLD are all issued before the first add
                 int kk = 0;
-                for (; kk + 8 <= ks; kk += 8) {
-                    float v[8];
+                for (; kk + FOLD <= ks; kk += FOLD) {
+                    float v[FOLD];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) v[q] = col[(kk + q) * wdt];
+                    for (int q = 0; q < FOLD; ++q) v[q] = col[(kk + q) * wdt];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) acc = acc + v[q];
+                    for (int q = 0; q < FOLD; ++q) acc = acc + v[q];
                 }
                 for (; kk < ks; ++kk) acc = acc + col[kk * wdt];
                 total[i] = acc;
