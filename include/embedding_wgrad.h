@@ -50,7 +50,8 @@ extern "C" {
 #endif
 
 /* Envelope (page, Data: MIN_TOKENS, MAX_TOKENS, _NROWS). MIN_TOKENS is the
- * first token count on PyTorch's sort-based path ("more than 3072 tokens"). */
+ * smallest token count that takes PyTorch's sort-based path (page,
+ * introduction: that path starts above 3072 tokens). */
 #define EWG_MIN_TOKENS 3073
 #define EWG_MAX_TOKENS 8192
 #define EWG_NROWS 10
@@ -103,12 +104,18 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
  * its content between calls is not part of the interface except for three
  * int32 words: the first 4 bytes (see below); the one at byte offset
  * EWG_WS_WAIT_TIMEOUTS_OFFSET, which counts the bounded waits inside the
- * kernel that gave up since the workspace was zero-filled (a diagnostic: no
- * wait is expected to give up; when one does, the call's result is wrong);
- * and the one at EWG_WS_STOLEN_SHARES_OFFSET, the number of shares of
- * long-run work that the last call's waiting workgroups took over from
- * workgroups that had not started (a diagnostic: 0 when all of the launch's
- * workgroups run together, and the result is the same either way).
+ * kernel that gave up since the workspace was zero-filled; and the one at
+ * EWG_WS_STOLEN_SHARES_OFFSET, the number of shares of long-run work that the
+ * last call's waiting workgroups took over from workgroups that had not
+ * started (a diagnostic: 0 when all of the launch's workgroups run together,
+ * and the result is the same either way).
+ *
+ * A wait that gives up is an ERROR of the call, not a diagnostic: the work
+ * behind it was skipped and that call's main_grad is wrong. Every wait is
+ * bounded (seconds) so that a launch always ends; none is expected to give up.
+ * A caller that must know reads the word before the call and after it has
+ * finished on its stream, and treats any growth as a failed call (the Python
+ * binding's checked mode does this and raises).
  * 0 if the sizes are out of range.
  */
 #define EWG_WS_WAIT_TIMEOUTS_OFFSET 144

@@ -14,7 +14,7 @@
  * _partial_sums_kernel and _long_run_sums_kernel. In this file's words:
  *
  *   1. The pairs (token id, position) are sorted; equal ids keep their
- *      positions in ascending order ("in position order").
+ *      positions in ascending order (introduction, first bullet).
  *   2. A run is the set of sorted slots holding one id. It is cut into chunks
  *      of NROWS = 10 rows, counted from the start of the run, so a run of at
  *      most 10 rows is one chunk.

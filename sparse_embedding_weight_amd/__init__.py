@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     MIN_TOKENS,
     NROWS,
     EmbeddingWgradError,
+    WaitGaveUpError,
     accumulate_embedding_wgrad,
     accumulate_embedding_wgrad_many_tokens,
     accumulate_embedding_wgrad_vocab_shard,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     new_many_tokens_workspace,
     new_workspace,
     position_bits,
+    raise_if_waits_gave_up,
     sort_tokens,
     stolen_shares,
     wait_timeouts,

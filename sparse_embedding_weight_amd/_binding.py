@@ -47,6 +47,8 @@ EXPORTS = (
     "accumulate_embedding_wgrad_many_tokens",
     "accumulate_embedding_wgrad_many_tokens_timed",
     "ewg_status_string",
+    # include/embedding_wgrad_test.h (test-only)
+    "ewg_test_accumulate_embedding_wgrad",
 )
 
 _i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -79,12 +81,18 @@ lib.accumulate_embedding_wgrad_many_tokens_timed.argtypes = _ACC_ARGS + [_vp]
 lib.accumulate_embedding_wgrad_many_tokens_timed.restype = _int
 lib.ewg_status_string.argtypes = [_int]
 lib.ewg_status_string.restype = ctypes.c_char_p
+lib.ewg_test_accumulate_embedding_wgrad.argtypes = _ACC_ARGS[:-1] + [_int, _int, _vp]
+lib.ewg_test_accumulate_embedding_wgrad.restype = _int
 
 
 class EmbeddingWgradError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
         super().__init__(f"{what}: {lib.ewg_status_string(status).decode()} (status {status})")
+
+
+class WaitGaveUpError(RuntimeError):
+    """A bounded wait inside the kernel gave up: the call's main_grad is wrong."""
 
 
 def position_bits(num_tokens: int) -> int:
@@ -164,7 +172,7 @@ def _workspace(n: int, hidden: int, device, workspace):
 
 
 def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor,
-                               workspace: torch.Tensor = None) -> None:
+                               workspace: torch.Tensor = None, checked: bool = False) -> None:
     """main_grad += embedding_dense_backward(grad, ids), touching only the rows of ids.
 
     ids: token ids, num_tokens elements (any shape, flattened row-major).
@@ -173,6 +181,9 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
     workspace: optional uint8 device tensor of >= workspace_bytes(num_tokens, hidden),
         zero-filled before its first use (new_workspace() makes one); by default a
         cached workspace per device and stream is used.
+    checked: synchronise after the call and raise WaitGaveUpError if a bounded wait
+        inside the kernel gave up during it (its result is then wrong). Off by
+        default: the unchecked call never synchronises.
     Requires can_accumulate_embedding_wgrad(ids, grad, main_grad); raises ValueError
     otherwise. Enqueued on the current stream of main_grad's device; no sync.
     """
@@ -182,6 +193,7 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
     n, hidden = ids.numel(), grad.shape[-1]
     ids_flat, grad2 = _flat_inputs(ids, grad)
     ws = _workspace(n, hidden, main_grad.device, workspace)
+    before = wait_timeouts(ws) if checked else 0
     with torch.cuda.device(main_grad.device):
         st = lib.accumulate_embedding_wgrad(
             ids_flat.data_ptr(), grad2.data_ptr(), main_grad.data_ptr(), n, hidden,
@@ -190,6 +202,29 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
             _stream_handle(main_grad.device))
     if st != EWG_OK:
         raise EmbeddingWgradError(st, "accumulate_embedding_wgrad")
+    if checked:
+        raise_if_waits_gave_up(ws, before, "accumulate_embedding_wgrad")
+
+
+def accumulate_with_grid_for_tests(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor,
+                              workspace: torch.Tensor, grid: int,
+                              defer_odd_shares: bool = False) -> None:
+    """Tests only (include/embedding_wgrad_test.h): accumulate_embedding_wgrad launched
+    with `grid` workgroups; with defer_odd_shares every odd workgroup leaves its long
+    share to the combine tasks. Same result as accumulate_embedding_wgrad."""
+    if not can_accumulate_embedding_wgrad(ids, grad, main_grad):
+        raise ValueError("accumulate_with_grid_for_tests: unsupported inputs")
+    n, hidden = ids.numel(), grad.shape[-1]
+    ids_flat, grad2 = _flat_inputs(ids, grad)
+    ws = _workspace(n, hidden, main_grad.device, workspace)
+    with torch.cuda.device(main_grad.device):
+        st = lib.ewg_test_accumulate_embedding_wgrad(
+            ids_flat.data_ptr(), grad2.data_ptr(), main_grad.data_ptr(), n, hidden,
+            main_grad.shape[0], grad2.stride(0), main_grad.stride(0), DTYPE_CODE[ids.dtype],
+            DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad.dtype], ws.data_ptr(), ws.numel(),
+            int(grid), 1 if defer_odd_shares else 0, _stream_handle(main_grad.device))
+    if st != EWG_OK:
+        raise EmbeddingWgradError(st, "ewg_test_accumulate_embedding_wgrad")
 
 
 def _same_layout(ids, grad, main_grad) -> bool:
@@ -352,3 +387,14 @@ def wait_timeouts(workspace: torch.Tensor) -> int:
     zero-filled (the documented diagnostic word; synchronises). Never expected."""
     o = WS_WAIT_TIMEOUTS_OFFSET
     return int(workspace[o:o + 4].view(torch.int32).item())
+
+
+def raise_if_waits_gave_up(workspace: torch.Tensor, before: int, what: str = "call") -> None:
+    """Raise WaitGaveUpError if the workspace's wait-timeout word grew past `before`
+    (its value read before the call): a wait that gave up skipped work, so the
+    call's result is wrong. Synchronises with the workspace's device."""
+    after = wait_timeouts(workspace)
+    if after != before:
+        raise WaitGaveUpError(
+            f"{what}: {after - before} bounded wait(s) inside the kernel gave up; "
+            "main_grad is wrong for this call")

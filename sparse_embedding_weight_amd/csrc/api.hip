@@ -3,10 +3,9 @@
 // Nothing here touches device memory or synchronises; every launch goes on
 // the caller's stream.
 #include "embedding_wgrad.h"
+#include "embedding_wgrad_test.h"
 
 #include <atomic>
-
-#include <cstdlib>
 
 #include "ewg_internal.h"
 
@@ -33,26 +32,6 @@ size_t float_size(int d) { return d == EWG_BF16 ? 2 : 4; }
 
 bool aligned(const void *p, int64_t row_stride_bytes, size_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a == 0) && (row_stride_bytes % (int64_t)a == 0);
-}
-
-// Workgroups of one launch: one per compute unit. The environment variable
-// EWG_GRID (2..4095) overrides it; the tests use that to run launches with
-// far fewer workgroups (long shares and many rounds per workgroup) and with
-// more than fit at once (combine tasks that take the long shares of
-// workgroups that have not started).
-int launch_grid(int cus) {
-    if (const char *e = getenv("EWG_GRID")) {
-        const long g = strtol(e, nullptr, 10);
-        if (g >= 2 && g <= kMaxGrid) return (int)g;
-    }
-    return cus;
-}
-
-// EWG_DEFER_ODD_SHARES=1 (tests only): the workgroups of odd number leave
-// their long shares to the combine tasks, which then take them over.
-int defer_odd_shares() {
-    const char *e = getenv("EWG_DEFER_ODD_SHARES");
-    return e && e[0] == '1' ? 1 : 0;
 }
 
 // Compute units of the current device, cached per device ordinal.
@@ -109,7 +88,7 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                int64_t hidden, int64_t num_embeddings, int64_t id_base, bool shard,
                int64_t grad_row_stride, int64_t main_grad_row_stride, int ids_dtype,
                int grad_dtype, int main_grad_dtype, void *workspace, size_t workspace_bytes,
-               hipStream_t stream, hipEvent_t *events) {
+               hipStream_t stream, hipEvent_t *events, int grid = 0, int defer_odd_shares = 0) {
     int st = shard ? (!is_known_dtype(ids_dtype) || !is_known_dtype(grad_dtype) ||
                               !is_known_dtype(main_grad_dtype)
                           ? EWG_INVALID_ARGUMENT
@@ -145,7 +124,7 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                                      (int)num_embeddings, id_base, shard, pos_bits, id_bits, grad,
                                      grad_row_stride,
                                      main_grad, main_grad_row_stride, (int)hidden, workspace, l,
-                                     launch_grid(num_cus()), next_epoch(), defer_odd_shares(),
+                                     grid > 0 ? grid : num_cus(), next_epoch(), defer_odd_shares,
                                      events ? events[2] : nullptr, events ? events[3] : nullptr,
                                      stream));
     if (st != EWG_OK) return st;
@@ -323,6 +302,21 @@ int accumulate_embedding_wgrad_many_tokens_timed(const void *ids, const void *gr
     return accumulate_many(ids, grad, main_grad, num_tokens, hidden, num_embeddings,
                            grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
                            main_grad_dtype, workspace, workspace_bytes, stream, events);
+}
+
+int ewg_test_accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_grad,
+                                        int64_t num_tokens, int64_t hidden,
+                                        int64_t num_embeddings, int64_t grad_row_stride,
+                                        int64_t main_grad_row_stride, int ids_dtype,
+                                        int grad_dtype, int main_grad_dtype, void *workspace,
+                                        size_t workspace_bytes, int grid, int defer_odd_shares,
+                                        hipStream_t stream) {
+    if (grid < 2 || grid > kMaxGrid || (defer_odd_shares != 0 && defer_odd_shares != 1))
+        return EWG_INVALID_ARGUMENT;
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
+                      grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                      main_grad_dtype, workspace, workspace_bytes, stream, nullptr, grid,
+                      defer_odd_shares);
 }
 
 const char *ewg_status_string(int status) {

@@ -1,14 +1,16 @@
 // The sort step as device code for one 1024-thread workgroup: packed
 // (id << pos_bits | position) keys sorted in LDS, runs of equal ids marked,
-// and the chunk table built in LDS. Used by the fused accumulate kernel (every
-// workgroup sorts the same keys, so no table crosses global memory) and by
-// the sort-only kernel that writes the tables out.
+// and the chunk table built in LDS. Used by the fused accumulate kernel (only
+// its workgroup 0 sorts; it publishes the long chunks and runs through the
+// workspace), by the many-token path's tile sort, and by the sort-only kernel
+// that writes the tables out.
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad":
 // _sort_tokens_kernel (sort the (token, position) pairs, give every sorted
 // slot the first and last slot of its run, list the runs longer than NROWS),
-// _position_bits, and the introduction ("sorts the token ids together with
-// their positions", rows summed "in position order").
+// _position_bits, and the introduction, first bullet (the ids are sorted with
+// their positions and each id's rows are summed in the order of those
+// positions).
 //
 // The keys enter in position order and every radix pass is stable, so
 // sorting on the id bits alone yields (id, position) order; the position bits

@@ -259,3 +259,43 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_checked_mode_raises_on_a_given_up_wait():
+    """The checked mode's test: a wait-timeout word that grew during the call
+    raises WaitGaveUpError; an unchanged one does not (CPU workspace, word preset)."""
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    o = B.WS_WAIT_TIMEOUTS_OFFSET
+    B.raise_if_waits_gave_up(ws, 0)
+    ws[o:o + 4].view(torch.int32)[0] = 3
+    with pytest.raises(B.WaitGaveUpError):
+        B.raise_if_waits_gave_up(ws, 0)
+    B.raise_if_waits_gave_up(ws, 3)
+    with pytest.raises(B.WaitGaveUpError):
+        B.raise_if_waits_gave_up(ws, 2)
+
+
+def test_test_entry_point_rejects_bad_launch_settings():
+    """ewg_test_accumulate_embedding_wgrad checks its grid (2..4095) and flag (0/1)
+    before anything else, and otherwise runs the normal argument checks."""
+    f = B.lib.ewg_test_accumulate_embedding_wgrad
+    # workspace address 8: not 256-byte aligned, so no call reaches a launch
+    args = [1, 1, 1, 8192, 7168, 129280, 7168, 7168, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
+            8, 1 << 30]
+    for grid, flag in ((1, 0), (4096, 0), (256, 2), (256, -1)):
+        assert f(*args, grid, flag, None) == B.EWG_INVALID_ARGUMENT
+    # a valid setting falls through to the normal checks: misaligned workspace
+    assert f(*args, 256, 0, None) == B.EWG_INVALID_ARGUMENT
+    # outside the envelope
+    bad = list(args)
+    bad[3] = 3072
+    assert f(*bad, 256, 0, None) == B.EWG_UNSUPPORTED
+
+
+def test_library_reads_no_environment_variable():
+    """The product library reads no environment variable (launch settings for
+    tests travel only through the test entry point's arguments)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    assert not re.search(r"\bgetenv\b", out), "libembedding_wgrad.so calls getenv"

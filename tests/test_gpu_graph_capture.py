@@ -16,7 +16,8 @@ from parity_util import _bits
 
 pytestmark = pytest.mark.gpu
 
-ewg = pytest.importorskip("sparse_embedding_weight_amd")
+# a missing or unloadable library fails the module (no skip)
+import sparse_embedding_weight_amd as ewg  # noqa: E402
 
 
 @pytest.fixture(autouse=True)

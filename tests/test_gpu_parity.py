@@ -16,7 +16,9 @@ from parity_util import _bits, assert_rows_match, oracle_rows  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-ewg = pytest.importorskip("sparse_embedding_weight_amd")
+# a missing or unloadable library fails the module (no skip)
+import sparse_embedding_weight_amd as ewg  # noqa: E402
+from sparse_embedding_weight_amd import _binding as B  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -81,8 +83,8 @@ def test_workload_full_size_bit_exact(name):
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_matches_torch_dense_embedding_backward(name):
     """A second, external reference: PyTorch-ROCm's aten::embedding_dense_backward
-    followed by main_grad.add_, the routine whose result the page's introduction says
-    the fused path reproduces for more than 3072 tokens. On the touched rows the two
+    followed by main_grad.add_, the routine whose result, per the page's introduction,
+    the fused path matches once a call has over 3072 tokens. On the touched rows the two
     agree bit for bit (NaNs compared as a class); rows of absent ids are not compared,
     since the dense path adds +0 to them."""
     w = wl.WORKLOADS[name]
@@ -407,37 +409,61 @@ def test_timed_entry_point_matches_plain_calls():
 
 @pytest.mark.parametrize("grid", ["2", "3", "16", "2x", "3x"])
 @pytest.mark.parametrize("name", ["zipf1.1_4096_v32000_h4096", "longrun_8192_v129280_h7168"])
-def test_launch_sizes(grid, name, monkeypatch):
-    """EWG_GRID sets the workgroups of a launch. With 2, 3 or 16 one follower
-    handles many rounds of short runs and a long share of many chunks; with two or
-    three times the compute units, workgroups that have not started hold long
-    shares that waiting combine tasks take over. The result stays bit-exact and
-    no bounded wait gives up."""
+def test_launch_sizes(grid, name):
+    """The test entry point sets the workgroups of a launch. With 2, 3 or 16 one
+    follower handles many rounds of short runs and a long share of many chunks;
+    with two or three times the compute units, workgroups that have not started
+    hold long shares that waiting combine tasks take over. The result stays
+    bit-exact and no bounded wait gives up."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     g = int(grid[:-1]) * cus if grid.endswith("x") else int(grid)
-    monkeypatch.setenv("EWG_GRID", str(g))
     w = wl.WORKLOADS[name]
     print(f"[launch size] {name} grid {g}", flush=True)
     ids = torch.from_numpy(wl.make_ids(w)).cuda()
     grad = wl.make_grad(w).cuda()
     mg = wl.make_main_grad(w, "cuda")
     ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
-    check_call(ids, grad, mg, workspace=ws)
+    rows = torch.unique(ids.reshape(-1).long())
+    before_rows, before = mg[rows].clone(), mg.clone()
+    B.accumulate_with_grid_for_tests(ids, grad, mg, ws, g)
+    torch.cuda.synchronize()
+    assert ewg.wait_timeouts(ws) == 0
+    assert_rows_match(ids, grad, mg, before, rows, before_rows)
 
 
 @pytest.mark.parametrize("name", ["zipf1.1_8192_v129280_h7168", "longrun_8192_v129280_h7168",
                                   "zipf1.3_4x2048_v129280_h7168_bf16mg"])
-def test_combine_takes_over_unclaimed_shares(name, monkeypatch):
-    """EWG_DEFER_ODD_SHARES makes every odd workgroup leave its long share
+def test_combine_takes_over_unclaimed_shares(name):
+    """The test entry point makes every odd workgroup leave its long share
     unclaimed, as a workgroup that cannot start would: the combine tasks that
     wait for those units take the shares over after a while. Bit-exact, no wait
     gives up, and the diagnostic word counts the shares taken over."""
-    monkeypatch.setenv("EWG_DEFER_ODD_SHARES", "1")
     w = wl.WORKLOADS[name]
     print(f"[taken-over shares] {name}", flush=True)
     ids = torch.from_numpy(wl.make_ids(w)).cuda()
     grad = wl.make_grad(w).cuda()
     mg = wl.make_main_grad(w, "cuda")
     ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
-    check_call(ids, grad, mg, workspace=ws)
+    rows = torch.unique(ids.reshape(-1).long())
+    before_rows, before = mg[rows].clone(), mg.clone()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B.accumulate_with_grid_for_tests(ids, grad, mg, ws, cus, defer_odd_shares=True)
+    torch.cuda.synchronize()
+    assert ewg.wait_timeouts(ws) == 0
+    assert_rows_match(ids, grad, mg, before, rows, before_rows)
     assert ewg.stolen_shares(ws) > 0
+
+
+def test_checked_call_passes_and_leaves_the_word():
+    """The checked mode synchronises after the call and raises only when a wait
+    gave up; a normal call leaves the word unchanged."""
+    w = wl.WORKLOADS["uniform3073_v512_h128"]
+    ids = torch.from_numpy(wl.make_ids(w)).cuda()
+    grad = wl.make_grad(w).cuda()
+    mg = wl.make_main_grad(w, "cuda")
+    ws = ewg.new_workspace(ids.numel(), w.hidden, "cuda")
+    rows = torch.unique(ids.reshape(-1).long())
+    before_rows, before = mg[rows].clone(), mg.clone()
+    ewg.accumulate_embedding_wgrad(ids, grad, mg, workspace=ws, checked=True)
+    assert ewg.wait_timeouts(ws) == 0
+    assert_rows_match(ids, grad, mg, before, rows, before_rows)

@@ -103,7 +103,7 @@ def test_round_bf16_hand_cases():
 # --------------------------------------------------------------------------
 # Sort tables: brute force without a sort (scan of the vocabulary) must give
 # the same sorted order, run bounds, long-run list and chunk starts
-# (_sort_tokens_kernel docstring; "in position order").
+# (_sort_tokens_kernel docstring; introduction, first bullet: ascending positions).
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seed", range(6))
