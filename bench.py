@@ -1,23 +1,26 @@
 """Benchmark of the embedding weight-gradient accumulation on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs all|none|A,B]
 
 One step = one whole call (one kernel: sort, chunk sums, single-chunk runs,
-ordered combine of long runs) over the headline workload: 8192 Zipf(1.1) token ids into a 129280 x 7168 fp32
-main_grad with a bf16 grad. Inputs are resident in HBM before timing. Before
-every step, outside its timed interval, a 1 GiB buffer is read (summed) so
-that neither L2 nor the 256 MB Infinity Cache holds the inputs; reading
-rather than writing leaves no dirty lines for the timed call to write back.
-Each step is timed with two HIP events that the library records on its
-launch stream right before and after the call (value, us_per_call). A second
-pass of the same steps dispatches the kernel with two more events of its own
-(roofline.achieved and us_per_launch: the kernel's execution alone, the figure
-a kernel trace shows); that pass is kept apart because such a dispatch adds
-time around the kernel.
+ordered combine of long runs) over the headline workload: 8192 Zipf(1.1)
+token ids into a 129280 x 7168 fp32 main_grad with a bf16 grad. Inputs are
+resident in HBM before timing. Before every step, outside its timed interval,
+a 1 GiB buffer is read (summed) so that neither L2 nor the 256 MB Infinity
+Cache holds the inputs; reading rather than writing leaves no dirty lines for
+the timed call to write back. Each step is timed with two HIP events that the
+library records on its launch stream right before and after the call (value,
+us_per_call). A second pass of the same steps dispatches the kernel with two
+more events of its own (roofline.achieved and us_per_launch: the kernel's
+execution alone, the figure a kernel trace shows); that pass is kept apart
+because such a dispatch adds time around the kernel.
 
 Prints one JSON line: value = algorithmic bytes / mean call time (GB/s), the
 roofline of the kernel (the whole call is one kernel), and the CPU oracle
-timed on the host as cpu_baseline. Also timed, each in its own object: the
+timed on the host as cpu_baseline (one thread, and every host thread over
+column blocks). Also, each in its own object: the same two passes on each of
+the five generated workloads (configs), the copy and read ceilings of a
+plain device copy and reduction timed in the same run (copy_ceiling), the
 dense PyTorch path on the same inputs (dense_baseline), the many-token entry
 point on a batch of more than 8192 tokens (many_tokens, with its own dense
 baseline), and with --vocab-shards S the vocabulary-shard entry point.
@@ -47,7 +50,14 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default=None)
+    p.add_argument("--workload", default=None,
+                   help="the headline workload (value and roofline); default the 8192-token "
+                        "Zipf(1.1) one")
+    p.add_argument("--configs", default="all",
+                   help="workloads timed under configs: all (default), none, or a comma list")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads of the all-core CPU oracle timing (default: OMP_NUM_THREADS, "
+                        "else the CPUs this process may run on)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="rough budget for the CPU oracle timing")
@@ -65,7 +75,7 @@ def parse_args():
     p.add_argument("--no-many-tokens", action="store_true",
                    help="skip timing the many-token entry point")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a 256 MiB device copy (reference for counter scaling)")
+                   help="also run a 256 MiB device fill (reference for counter scaling)")
     return p.parse_args()
 
 
@@ -121,9 +131,33 @@ def measured_traffic(workload_name):
     return int(val.group(1))
 
 
-def cpu_baseline(w, ids_np, grad_np, budget_s):
-    """The oracle as it stands (single-threaded C), on the whole workload with
-    main_grad restricted to its touched rows (ids relabelled in order)."""
+def host_threads(requested):
+    """Threads of the all-core CPU timing: --cpu-threads, else OMP_NUM_THREADS, else the
+    CPUs this process may run on."""
+    if requested > 0:
+        return requested
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return min(int(env), len(os.sched_getaffinity(0)))
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, ids_np, grad_np, budget_s, threads):
+    """The oracle as it stands, on the whole workload with main_grad restricted to its
+    touched rows (ids relabelled in order): median seconds per call of the serial C
+    routine, and of the same routine run at once on `threads` column blocks (each
+    column's arithmetic is independent, so the bits are the serial call's)."""
     import oracle
     import workloads as wl
 
@@ -132,14 +166,50 @@ def cpu_baseline(w, ids_np, grad_np, budget_s):
     rng = np.random.default_rng(0)
     mg = wl.to_numpy_bits(wl.normal_tensor(rng, (rows.size, w.hidden), w.main_grad_sigma,
                                            w.main_grad_dtype))
-    times = []
-    start = time.perf_counter()
-    while not times or (time.perf_counter() - start < budget_s and len(times) < 20):
-        m = mg.copy()
-        t0 = time.perf_counter()
-        oracle.accumulate_embedding_wgrad(compact, grad_np, m, w.grad_dtype, w.main_grad_dtype)
-        times.append(time.perf_counter() - t0)
-    return float(np.median(times)), len(times)
+
+    def median_time(call):
+        times = []
+        start = time.perf_counter()
+        while not times or (time.perf_counter() - start < budget_s / 2 and len(times) < 20):
+            m = mg.copy()
+            t0 = time.perf_counter()
+            call(m)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    serial = median_time(lambda m: oracle.accumulate_embedding_wgrad(
+        compact, grad_np, m, w.grad_dtype, w.main_grad_dtype))
+    blocks = []
+    threaded = median_time(lambda m: blocks.append(oracle.accumulate_embedding_wgrad_column_blocks(
+        compact, grad_np, m, w.grad_dtype, w.main_grad_dtype, threads)))
+    return serial, threaded, blocks[-1]
+
+
+def copy_ceiling(torch, dev, reps=10):
+    """Device bandwidth ceilings measured in this run (context for the roofline, never
+    its peak): a 1 GiB device-to-device tensor copy (bytes read + written per second)
+    and a 1 GiB fp32 sum (bytes read per second), each the best of `reps`, timed with
+    events on the current stream."""
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    out = {}
+    for kind, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 << 30),
+                             ("read", lambda: sink.copy_(src.sum()), 1 << 30)):
+        best = None
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[kind] = round(nbytes / (best * 1e-3) / 1e9, 1)
+    del src, dst
+    return {"copy_ceiling_GBps": out["copy"], "read_ceiling_GBps": out["read"],
+            "kind": "torch copy_ of 1 GiB (read + write bytes) and torch sum of 1 GiB fp32 "
+                    "(read bytes), best of %d, HIP events" % reps}
 
 
 def time_vocab_shards(torch, ewg, wl, w, ids, ids_np, grad, mg, flush, flush_sink, flush_mode,
@@ -254,6 +324,96 @@ def time_many_tokens(torch, ewg, B, wl, name, hip, flush, flush_sink, flush_mode
     return out
 
 
+class Workload:
+    """One generated workload resident on the device, with its call arguments."""
+
+    def __init__(self, torch, ewg, B, wl, name, dev):
+        w = self.w = wl.WORKLOADS[name]
+        self.name = name
+        self.ids_np = wl.make_ids(w).reshape(-1)
+        self.ids = torch.from_numpy(self.ids_np).to(dev)
+        self.grad_cpu = wl.make_grad(w).reshape(w.num_tokens, w.hidden)
+        self.grad = self.grad_cpu.to(dev)
+        self.mg = wl.make_main_grad(w, dev)
+        counts = np.bincount(self.ids_np, minlength=w.vocab)
+        self.uniq = int((counts > 0).sum())
+        self.u_long = int((counts > ewg.NROWS).sum())
+        self.alg_bytes = wl.algorithmic_bytes(w.num_tokens, w.hidden, self.uniq, w.grad_dtype,
+                                              w.main_grad_dtype, self.ids_np.itemsize)
+        self.ws = ewg.new_workspace(w.num_tokens, w.hidden, dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        self.call_args = (self.ids.data_ptr(), self.grad.data_ptr(), self.mg.data_ptr(),
+                          w.num_tokens, w.hidden, w.vocab, self.grad.stride(0), self.mg.stride(0),
+                          B.DTYPE_CODE[self.ids.dtype], B.DTYPE_CODE[self.grad.dtype],
+                          B.DTYPE_CODE[self.mg.dtype], self.ws.data_ptr(), self.ws.numel(), stream)
+
+    def describe(self):
+        w = self.w
+        return {"workload": self.name, "num_tokens": w.num_tokens, "vocab": w.vocab,
+                "hidden": w.hidden,
+                "ids": f"{w.ids_kind}" + (f"(s={w.zipf_s})" if w.ids_kind == "zipf" else ""),
+                "grad_dtype": w.grad_dtype, "main_grad_dtype": w.main_grad_dtype,
+                "distinct_ids": self.uniq, "runs_longer_than_10": self.u_long,
+                "algorithmic_bytes": self.alg_bytes}
+
+
+def timed_pass(torch, B, hip, work, args, flush, flush_sink, kernel_events):
+    """warmup + steps calls of one workload; per timed call the (call, kernel)
+    durations in ms and the wall time of the timed steps. Without kernel_events the
+    kernel is dispatched plainly (slots 2, 3 NULL): a dispatch that takes its own
+    events costs extra time around it."""
+    nsteps = args.warmup + args.steps
+    events = [hip.create(4 if kernel_events else 2) for _ in range(nsteps)]
+    slots = [(ctypes.c_void_p * 4)(*(list(e) + [None, None])[:4]) for e in events]
+    torch.cuda.synchronize()
+    t0 = None
+    for step in range(nsteps):
+        if step == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        if args.flush == "read":
+            flush_sink.copy_(flush.sum())
+        elif args.flush == "write":
+            flush.fill_(float(step))
+        st = B.lib.accumulate_embedding_wgrad_timed(*work.call_args, slots[step])
+        if st != 0:
+            raise B.EmbeddingWgradError(st, "accumulate_embedding_wgrad_timed")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = events[args.warmup:]
+    calls = np.array([hip.ms(e[0], e[1]) for e in timed])
+    kernels = np.array([hip.ms(e[2], e[3]) for e in timed]) if kernel_events else None
+    for e in events:
+        hip.destroy(e)
+    return calls, kernels, elapsed
+
+
+def pct(t):
+    return [round(float(np.percentile(t, q)) * 1e3, 2) for q in (10, 50, 90)]
+
+
+def measure(torch, ewg, B, hip, work, args, flush, flush_sink):
+    """The two passes on one workload: plain dispatches between the call's own events
+    (us_per_call, GB_per_s), then dispatches with the kernel's own events
+    (us_per_launch and the roofline fraction). Raises if a bounded wait gave up."""
+    t_call, _, wall = timed_pass(torch, B, hip, work, args, flush, flush_sink, False)
+    _, t_kernel, _ = timed_pass(torch, B, hip, work, args, flush, flush_sink, True)
+    timeouts = ewg.wait_timeouts(work.ws)
+    if timeouts:
+        raise RuntimeError(f"{timeouts} bounded waits gave up inside the kernel ({work.name})")
+    call_ms, kernel_ms = float(t_call.mean()), float(t_kernel.mean())
+    kernel_gbs = work.alg_bytes / (kernel_ms * 1e-3) / 1e9
+    rec = work.describe()
+    rec.update({
+        "us_per_call": round(call_ms * 1e3, 2), "us_per_call_p10_p50_p90": pct(t_call),
+        "GB_per_s": round(work.alg_bytes / (call_ms * 1e-3) / 1e9, 1),
+        "us_per_launch": round(kernel_ms * 1e3, 2), "us_per_launch_p10_p50_p90": pct(t_kernel),
+        "kernel_GB_per_s": round(kernel_gbs, 1), "frac": round(kernel_gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(work.name),
+    })
+    return rec, call_ms, kernel_ms, wall
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -268,79 +428,41 @@ def main():
     import workloads as wl
 
     name = args.workload or wl.HEADLINE
-    w = wl.WORKLOADS[name]
+    if name not in wl.WORKLOADS:
+        raise SystemExit(f"unknown workload {name!r}; known: {', '.join(wl.WORKLOADS)}")
+    if args.configs == "all":
+        config_names = list(wl.WORKLOADS)
+    elif args.configs == "none":
+        config_names = []
+    else:
+        config_names = args.configs.split(",")
+        for c in config_names:
+            if c not in wl.WORKLOADS:
+                raise SystemExit(f"unknown workload {c!r} in --configs")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    ids_np = wl.make_ids(w).reshape(-1)
-    ids = torch.from_numpy(ids_np).to(dev)
-    grad_cpu = wl.make_grad(w).reshape(w.num_tokens, w.hidden)
-    grad = grad_cpu.to(dev)
-    mg = wl.make_main_grad(w, dev)
-    counts = np.bincount(ids_np, minlength=w.vocab)
-    uniq = int((counts > 0).sum())
-    u_long = int((counts > ewg.NROWS).sum())
-    alg_bytes = wl.algorithmic_bytes(w.num_tokens, w.hidden, uniq, w.grad_dtype,
-                                     w.main_grad_dtype, ids_np.itemsize)
-
-    ws = ewg.new_workspace(w.num_tokens, w.hidden, dev)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     hip = HipEvents()
-    nsteps = args.warmup + args.steps
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    call_args = (ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), w.num_tokens, w.hidden, w.vocab,
-                 grad.stride(0), mg.stride(0), B.DTYPE_CODE[ids.dtype], B.DTYPE_CODE[grad.dtype],
-                 B.DTYPE_CODE[mg.dtype], ws.data_ptr(), ws.numel(), stream)
 
-    def timed_pass(kernel_events):
-        """warmup + steps calls; per timed call the (call, kernel) durations in ms.
-        Without kernel_events the kernel is dispatched plainly (slots 2, 3 NULL):
-        a dispatch that takes its own events costs extra time around it."""
-        events = [hip.create(4 if kernel_events else 2) for _ in range(nsteps)]
-        slots = [(ctypes.c_void_p * 4)(*(list(e) + [None, None])[:4]) for e in events]
-        torch.cuda.synchronize()
-        t0 = None
-        for step in range(nsteps):
-            if step == args.warmup:
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-            if args.flush == "read":
-                flush_sink.copy_(flush.sum())
-            elif args.flush == "write":
-                flush.fill_(float(step))
-            st = B.lib.accumulate_embedding_wgrad_timed(*call_args, slots[step])
-            if st != 0:
-                raise B.EmbeddingWgradError(st, "accumulate_embedding_wgrad_timed")
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        timed = events[args.warmup:]
-        calls = np.array([hip.ms(e[0], e[1]) for e in timed])
-        kernels = np.array([hip.ms(e[2], e[3]) for e in timed]) if kernel_events else None
-        for e in events:
-            hip.destroy(e)
-        return calls, kernels, elapsed
-
-    # value and us_per_call: plain dispatches between the call's own events
-    t_call, _, wall = timed_pass(False)
-    # roofline: the kernel's execution alone, from events its dispatch takes
-    _, t_kernel, _ = timed_pass(True)
-    timeouts = ewg.wait_timeouts(ws)
-    if timeouts:
-        raise RuntimeError(f"{timeouts} bounded waits gave up inside the kernel")
+    # the headline workload: value and roofline
+    work = Workload(torch, ewg, B, wl, name, dev)
+    w = work.w
+    head, mean_call_ms, mean_kernel_ms, wall = measure(torch, ewg, B, hip, work, args, flush,
+                                                       flush_sink)
+    value = work.alg_bytes / (mean_call_ms * 1e-3) / 1e9
+    achieved = work.alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        buf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         for _ in range(3):
-            dst.copy_(src)
+            buf.fill_(1)
         torch.cuda.synchronize()
+        del buf
 
-    mean_call_ms = float(t_call.mean())
-    value = alg_bytes / (mean_call_ms * 1e-3) / 1e9
-    mean_kernel_ms = float(t_kernel.mean())
-    achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
-
+    cfg = work.describe()
+    cfg["cache_flush_between_calls"] = args.flush
     result = {
         "metric": "us/call + achieved HBM GB/s, 8192 tokens into 129280x7168 main_grad",
         "value": round(value, 1),
@@ -349,34 +471,49 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(mean_call_ms, 5),
-        "us_per_call": round(mean_call_ms * 1e3, 2),
-        "us_per_call_p10_p50_p90": [round(float(np.percentile(t_call, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "us_per_call": head["us_per_call"],
+        "us_per_call_p10_p50_p90": head["us_per_call_p10_p50_p90"],
         "wall_ms_per_step_incl_cache_flush": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{w.grad_dtype}->{w.main_grad_dtype}",
         "data": "synthetic",
-        "config": {"workload": name, "num_tokens": w.num_tokens, "vocab": w.vocab,
-                   "hidden": w.hidden, "ids": f"{w.ids_kind}" + (f"(s={w.zipf_s})" if w.ids_kind == "zipf" else ""),
-                   "grad_dtype": w.grad_dtype, "main_grad_dtype": w.main_grad_dtype,
-                   "distinct_ids": uniq, "runs_longer_than_10": u_long,
-                   "algorithmic_bytes": alg_bytes, "cache_flush_between_calls": args.flush},
+        "config": cfg,
         "roofline": {"bound": "hbm", "kernel": "accumulate_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "us_per_launch": round(mean_kernel_ms * 1e3, 2),
-                     "traffic": measured_traffic(name)},
+                     "algorithmic_bytes_per_launch": work.alg_bytes,
+                     "us_per_launch": head["us_per_launch"],
+                     "traffic": head["traffic"]},
     }
 
     if args.vocab_shards > 1:
-        result["vocab_shards"] = time_vocab_shards(torch, ewg, wl, w, ids, ids_np, grad, mg, flush,
-                                                   flush_sink, args.flush, args.vocab_shards,
-                                                   args.steps, args.warmup)
+        result["vocab_shards"] = time_vocab_shards(torch, ewg, wl, w, work.ids, work.ids_np,
+                                                   work.grad, work.mg, flush, flush_sink,
+                                                   args.flush, args.vocab_shards, args.steps,
+                                                   args.warmup)
 
     if not args.no_dense_baseline:
-        result["dense_baseline"] = dense_baseline(torch, w, ids, grad, mg, flush, flush_sink,
-                                                  args.flush, mean_call_ms)
+        result["dense_baseline"] = dense_baseline(torch, w, work.ids, work.grad, work.mg, flush,
+                                                  flush_sink, args.flush, mean_call_ms)
+    ids_np, grad_cpu = work.ids_np, work.grad_cpu
+    del work
+    torch.cuda.empty_cache()
+
+    # every generated workload (the headline's record is the one measured above)
+    if config_names:
+        configs = []
+        for c in config_names:
+            if c == name:
+                configs.append(head)
+                continue
+            cw = Workload(torch, ewg, B, wl, c, dev)
+            configs.append(measure(torch, ewg, B, hip, cw, args, flush, flush_sink)[0])
+            del cw
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+
+    result["copy_ceiling"] = copy_ceiling(torch, dev)
 
     if not args.no_many_tokens:
         result["many_tokens"] = time_many_tokens(
@@ -384,14 +521,25 @@ def main():
             args.flush, args.steps, args.warmup, not args.no_dense_baseline)
 
     if not args.no_cpu_baseline:
-        t_cpu, reps = cpu_baseline(w, ids_np, wl.to_numpy_bits(grad_cpu), args.cpu_seconds)
+        threads = host_threads(args.cpu_threads)
+        (t1, r1), (tn, rn), blocks = cpu_baseline(w, ids_np, wl.to_numpy_bits(grad_cpu),
+                                                  args.cpu_seconds, threads)
         result["cpu_baseline"] = {
-            "value": round(alg_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds_per_call": round(t_cpu, 4),
+            "value": round(alg_bytes_of(result) / tn / 1e9, 3), "unit": "GB/s", "cores": blocks,
+            "kind": "oracle", "seconds_per_call": round(tn, 4),
+            "one_core": {"value": round(alg_bytes_of(result) / t1 / 1e9, 3), "unit": "GB/s",
+                         "seconds_per_call": round(t1, 4), "calls": r1},
+            "cpu_model": cpu_model(),
             "sample": f"the whole workload ({w.num_tokens} tokens, hidden {w.hidden}); main_grad "
-                      f"restricted to its {uniq} touched rows (ids relabelled in order); median of "
-                      f"{reps} calls of the single-threaded C oracle"}
+                      f"restricted to its {result['config']['distinct_ids']} touched rows (ids "
+                      f"relabelled in order); median of {rn} calls of the C oracle run at once "
+                      f"on {blocks} column blocks, one thread each (one_core: median of {r1} "
+                      f"serial calls)"}
     print(json.dumps(result), flush=True)
+
+
+def alg_bytes_of(result):
+    return result["config"]["algorithmic_bytes"]
 
 
 if __name__ == "__main__":

@@ -263,7 +263,10 @@ int accumulate_embedding_wgrad_sort_tokens(const void *ids, int64_t num_tokens,
  * accumulate_embedding_wgrad_many_tokens_workspace_bytes: bytes of workspace
  *   for these sizes (0 if out of range). The workspace needs no clearing:
  *   a call writes every part of it before reading it. Its first int32 is the
- *   invalid-id count, as for accumulate_embedding_wgrad.
+ *   invalid-id count, as for accumulate_embedding_wgrad. A many-token call
+ *   writes nothing in bytes 128..1023, where accumulate_embedding_wgrad keeps
+ *   its flags and counters, so one buffer (large enough for both) may be
+ *   passed to either entry point in turn.
  * accumulate_embedding_wgrad_many_tokens: arguments, layouts, the id rule
  *   (an id outside [0, num_embeddings) makes the call change nothing in
  *   main_grad and stores the number of such ids in the first int32 of the

@@ -133,3 +133,31 @@ def accumulate_embedding_wgrad(ids: np.ndarray, grad: np.ndarray, main_grad: np.
         _ptr(main_grad), m_flag, _row_stride(main_grad, "main_grad"), grad.shape[1])
     if rc != 0:
         raise MemoryError("oracle_accumulate_embedding_wgrad ran out of memory")
+
+
+def accumulate_embedding_wgrad_column_blocks(ids: np.ndarray, grad: np.ndarray,
+                                             main_grad: np.ndarray, grad_dtype: str,
+                                             main_grad_dtype: str, threads: int) -> int:
+    """accumulate_embedding_wgrad with the columns cut into `threads` blocks, each
+    block one call of the same C routine on column views of grad and main_grad,
+    the calls running at once on threads (ctypes drops the GIL during a call).
+
+    Every sum of the page's arithmetic runs down one column (one element of the
+    hidden dimension), so a block's columns see exactly the operations, in
+    exactly the order, of the whole call: the result is the serial one bit for
+    bit (pinned in tests/test_oracle_pins.py). Returns the number of blocks."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hidden = grad.shape[1]
+    threads = max(1, min(int(threads), hidden))
+    # block edges on multiples of 16 columns (64 bytes of fp32) where the width allows
+    step = -(-hidden // threads)
+    step = -(-step // 16) * 16 if hidden >= 16 * threads else step
+    edges = list(range(0, hidden, step)) + [hidden]
+    blocks = list(zip(edges[:-1], edges[1:]))
+    with ThreadPoolExecutor(max_workers=len(blocks)) as pool:
+        futures = [pool.submit(accumulate_embedding_wgrad, ids, grad[:, a:b], main_grad[:, a:b],
+                               grad_dtype, main_grad_dtype) for a, b in blocks]
+        for f in futures:
+            f.result()
+    return len(blocks)

@@ -116,13 +116,16 @@ constexpr int kManyMaxTiles = kManyMaxTokens / kMaxTokens;  // tiles of one LDS 
 
 // First bytes of the workspace of a many-token call. The first int32 is the
 // invalid-id count, as in the one-kernel workspace; the rest is written by
-// every call before it is read.
+// every call before it is read. It lies in line 0 of WsHeader (host-read
+// counts only), and the many-token arrays start after the whole WsHeader, so
+// a many-token call never touches the one-kernel path's flags and counters
+// (lines 1-7) and one buffer may serve both paths in turn.
 struct ManyHeader {
     int32_t invalid_ids;
     uint32_t n_chunks, n_long_runs, n_long_chunks, n_tasks;
     int32_t tile_bad[kManyMaxTiles];   // invalid ids per tile
 };
-static_assert(sizeof(ManyHeader) <= 256, "many-token header fits its 256 bytes");
+static_assert(sizeof(ManyHeader) <= 128, "many-token header fits line 0 of WsHeader");
 
 struct ManyLayout {
     size_t tkeys;            // uint32 per position: each tile's keys, sorted
@@ -142,7 +145,7 @@ inline ManyLayout many_layout(int64_t num_tokens, int64_t hidden) {
     const size_t tiles = (n + kMaxTokens - 1) / kMaxTokens;
     l.max_long_chunks = 2 * num_tokens / 11;
     l.max_long_runs = num_tokens / 11;
-    l.tkeys = 256;
+    l.tkeys = sizeof(WsHeader);
     l.gpos = round_up(l.tkeys + 4 * tiles * kMaxTokens, 256);
     l.gid = round_up(l.gpos + 4 * n, 256);
     l.cw = round_up(l.gid + 4 * n, 256);

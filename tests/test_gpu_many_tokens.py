@@ -207,3 +207,24 @@ def test_many_invalid_ids_change_nothing():
         assert ewg.invalid_id_count(ws) == 2
     check_many(ids, grad, mg, workspace=ws)
     assert ewg.invalid_id_count(ws) == 0
+
+
+def test_one_buffer_serves_both_paths():
+    """One zero-filled buffer, large enough for both entry points, passed to the
+    one-kernel path and the many-token path in turn: the many-token call leaves the
+    one-kernel path's flags and counters alone, so every call stays bit-exact and
+    no bounded wait gives up."""
+    hidden = 512
+    need = max(ewg.workspace_bytes(8192, hidden),
+               ewg.many_tokens_workspace_bytes(20000, hidden))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i in range(2):
+        print(f"[shared workspace] round {i}: one-kernel call", flush=True)
+        ids, grad, mg = make_case(8192, 3000, hidden, seed=40 + i)
+        rows = torch.unique(ids.long())
+        before, before_rows = mg.clone(), mg[rows].clone()
+        ewg.accumulate_embedding_wgrad(ids, grad, mg, workspace=ws, checked=True)
+        torch.cuda.synchronize()
+        assert_rows_match(ids, grad, mg, before, rows, before_rows)
+        print(f"[shared workspace] round {i}: many-token call", flush=True)
+        check_many(*make_case(20000, 5000, hidden, seed=50 + i), workspace=ws)

@@ -319,6 +319,21 @@ def test_column_slices_are_independent():
         assert np.array_equal(part, full[:, lo:hi])
 
 
+@pytest.mark.parametrize("grad_dtype,mg_dtype", [("bf16", "fp32"), ("fp32", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("hidden,threads", [(7, 8), (40, 3), (100, 8), (257, 5), (64, 1)])
+def test_column_blocks_equal_serial(grad_dtype, mg_dtype, hidden, threads):
+    """The threaded timing entry (column blocks, one call of the C routine each, run at
+    once) gives the serial call's bits, for ragged widths and more threads than columns."""
+    rng = np.random.default_rng(18 + hidden)
+    ids, grad, mg = random_problem(rng, 3100, 50, hidden, grad_dtype, mg_dtype)
+    serial, blocked = mg.copy(), mg.copy()
+    oracle.accumulate_embedding_wgrad(ids, grad, serial, grad_dtype, mg_dtype)
+    blocks = oracle.accumulate_embedding_wgrad_column_blocks(ids, grad, blocked, grad_dtype,
+                                                             mg_dtype, threads)
+    assert 1 <= blocks <= min(threads, hidden)
+    assert np.array_equal(blocked.view(np.uint8), serial.view(np.uint8))
+
+
 def test_row_strides_and_int64_ids():
     rng = np.random.default_rng(16)
     n, vocab, hidden = 500, 20, 10
