@@ -69,7 +69,8 @@ typedef enum ewg_status {
     EWG_UNSUPPORTED = 1,          /* outside the envelope (can_accumulate... is 0) */
     EWG_INVALID_ARGUMENT = 2,     /* null pointer, bad stride, bad dtype code */
     EWG_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below ..._workspace_bytes() */
-    EWG_HIP_ERROR = 4             /* a kernel launch failed */
+    EWG_HIP_ERROR = 4,            /* a kernel launch failed */
+    EWG_SCRATCH_TOO_SMALL = 5     /* ..._no_alloc: sizes beyond EWG_NO_ALLOC_SCRATCH_BYTES */
 } ewg_status;
 
 /*
@@ -168,6 +169,33 @@ int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_gra
                                int64_t grad_row_stride, int64_t main_grad_row_stride,
                                int ids_dtype, int grad_dtype, int main_grad_dtype,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * accumulate_embedding_wgrad (same arguments less the workspace, same checks,
+ * arithmetic and result) with the workspace in a static device array of
+ * EWG_NO_ALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends (its address is looked up once per device,
+ * on that device's first call). The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine. It enqueues on `stream` a small
+ * kernel that zeroes the array's header, then the accumulate kernel.
+ *
+ * Every call on one device shares that device's array and leaves its contents
+ * there: calls that overlap on one device (on different streams, or from
+ * different threads without ordering) race and give wrong results. Sizes
+ * whose workspace (accumulate_embedding_wgrad_workspace_bytes) exceeds
+ * EWG_NO_ALLOC_SCRATCH_BYTES return EWG_SCRATCH_TOO_SMALL before anything is
+ * enqueued; 64 MiB holds 8192 tokens up to hidden 11008. A bounded wait that
+ * gives up is not reported by this entry point (use accumulate_embedding_wgrad
+ * with a workspace to read the count).
+ */
+#define EWG_NO_ALLOC_SCRATCH_BYTES (64 << 20)
+int accumulate_embedding_wgrad_no_alloc(const void *ids, const void *grad, void *main_grad,
+                                        int64_t num_tokens, int64_t hidden,
+                                        int64_t num_embeddings, int64_t grad_row_stride,
+                                        int64_t main_grad_row_stride, int ids_dtype,
+                                        int grad_dtype, int main_grad_dtype, hipStream_t stream);
 
 /*
  * accumulate_embedding_wgrad with timing markers: `events` points to 4

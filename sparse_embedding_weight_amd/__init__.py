@@ -12,11 +12,13 @@ from ._binding import (  # noqa: F401
     MANY_MAX_TOKENS,
     MAX_TOKENS,
     MIN_TOKENS,
+    NO_ALLOC_SCRATCH_BYTES,
     NROWS,
     EmbeddingWgradError,
     WaitGaveUpError,
     accumulate_embedding_wgrad,
     accumulate_embedding_wgrad_many_tokens,
+    accumulate_embedding_wgrad_no_alloc,
     accumulate_embedding_wgrad_vocab_shard,
     can_accumulate_embedding_wgrad,
     can_accumulate_embedding_wgrad_many_tokens,

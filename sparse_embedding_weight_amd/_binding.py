@@ -27,7 +27,9 @@ MANY_MAX_TOKENS = 131072          # EWG_MANY_MAX_TOKENS
 MANY_MAX_EMBEDDINGS = 262144      # EWG_MANY_MAX_EMBEDDINGS
 
 EWG_INT32, EWG_INT64, EWG_BF16, EWG_FP32 = 0, 1, 2, 3
-EWG_OK, EWG_UNSUPPORTED, EWG_INVALID_ARGUMENT, EWG_WORKSPACE_TOO_SMALL, EWG_HIP_ERROR = range(5)
+(EWG_OK, EWG_UNSUPPORTED, EWG_INVALID_ARGUMENT, EWG_WORKSPACE_TOO_SMALL, EWG_HIP_ERROR,
+ EWG_SCRATCH_TOO_SMALL) = range(6)
+NO_ALLOC_SCRATCH_BYTES = 64 << 20  # EWG_NO_ALLOC_SCRATCH_BYTES
 
 DTYPE_CODE = {torch.int32: EWG_INT32, torch.int64: EWG_INT64,
               torch.bfloat16: EWG_BF16, torch.float32: EWG_FP32}
@@ -39,6 +41,7 @@ EXPORTS = (
     "accumulate_embedding_wgrad_workspace_bytes",
     "accumulate_embedding_wgrad",
     "accumulate_embedding_wgrad_timed",
+    "accumulate_embedding_wgrad_no_alloc",
     "can_accumulate_embedding_wgrad_vocab_shard",
     "accumulate_embedding_wgrad_vocab_shard",
     "accumulate_embedding_wgrad_sort_tokens",
@@ -64,6 +67,8 @@ lib.accumulate_embedding_wgrad.argtypes = _ACC_ARGS
 lib.accumulate_embedding_wgrad.restype = _int
 lib.accumulate_embedding_wgrad_timed.argtypes = _ACC_ARGS + [_vp]
 lib.accumulate_embedding_wgrad_timed.restype = _int
+lib.accumulate_embedding_wgrad_no_alloc.argtypes = _ACC_ARGS[:11] + [_vp]
+lib.accumulate_embedding_wgrad_no_alloc.restype = _int
 lib.can_accumulate_embedding_wgrad_vocab_shard.argtypes = [_i64, _i64, _i64, _i64, _int, _int, _int]
 lib.can_accumulate_embedding_wgrad_vocab_shard.restype = _int
 lib.accumulate_embedding_wgrad_vocab_shard.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
@@ -204,6 +209,36 @@ def accumulate_embedding_wgrad(ids: torch.Tensor, grad: torch.Tensor, main_grad:
         raise EmbeddingWgradError(st, "accumulate_embedding_wgrad")
     if checked:
         raise_if_waits_gave_up(ws, before, "accumulate_embedding_wgrad")
+
+
+def accumulate_embedding_wgrad_no_alloc(ids: torch.Tensor, grad: torch.Tensor,
+                                        main_grad: torch.Tensor) -> None:
+    """accumulate_embedding_wgrad without a workspace and without allocating: the
+    library's static per-device scratch serves as the workspace (calls that overlap
+    on one device race). Nothing is copied either, so ids must be contiguous and
+    grad viewable as [num_tokens, hidden] with unit column stride; raises ValueError
+    otherwise, and EmbeddingWgradError (EWG_SCRATCH_TOO_SMALL) for sizes whose
+    workspace exceeds NO_ALLOC_SCRATCH_BYTES. Enqueued on the current stream."""
+    if not can_accumulate_embedding_wgrad(ids, grad, main_grad):
+        raise ValueError("accumulate_embedding_wgrad_no_alloc: unsupported inputs "
+                         "(see can_accumulate_embedding_wgrad)")
+    n, hidden = ids.numel(), grad.shape[-1]
+    if not ids.is_contiguous():
+        raise ValueError("accumulate_embedding_wgrad_no_alloc: ids must be contiguous")
+    try:
+        grad2 = grad.view(n, hidden)
+    except RuntimeError:
+        raise ValueError("accumulate_embedding_wgrad_no_alloc: grad must be viewable as "
+                         "[num_tokens, hidden]") from None
+    if grad2.stride(1) != 1:
+        raise ValueError("accumulate_embedding_wgrad_no_alloc: grad needs unit column stride")
+    with torch.cuda.device(main_grad.device):
+        st = lib.accumulate_embedding_wgrad_no_alloc(
+            ids.data_ptr(), grad2.data_ptr(), main_grad.data_ptr(), n, hidden,
+            main_grad.shape[0], grad2.stride(0), main_grad.stride(0), DTYPE_CODE[ids.dtype],
+            DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad.dtype], _stream_handle(main_grad.device))
+    if st != EWG_OK:
+        raise EmbeddingWgradError(st, "accumulate_embedding_wgrad_no_alloc")
 
 
 def accumulate_with_grid_for_tests(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor,

@@ -6,6 +6,7 @@
 #include "embedding_wgrad_test.h"
 
 #include <atomic>
+#include <mutex>
 
 #include "ewg_internal.h"
 
@@ -166,6 +167,43 @@ int accumulate_many(const void *ids, const void *grad, void *main_grad, int64_t 
     return EWG_OK;
 }
 
+// ---- the entry point that allocates nothing ----------------------------------
+
+// Workspace of accumulate_embedding_wgrad_no_alloc: one array on every device
+// the library runs on, held until the process ends. On the host this name is
+// only a stand-in for the symbol; host code uses the device address that
+// hipGetSymbolAddress returns for the current device, never the name.
+static __device__ __align__(256) uint8_t scratch[EWG_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device: looked up once per
+// device, with that device current, and kept. nullptr if the lookup fails.
+void *scratch_address() {
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        addr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+constexpr int kHeaderWords = (int)(sizeof(WsHeader) / sizeof(uint32_t));
+static_assert(kHeaderWords <= 1024, "one workgroup clears the header");
+
+// Zeroes the workspace header: the flag, tickets and counters a call starts
+// from. A kernel rather than a memset node, so the call may be captured.
+__global__ void clear_header_kernel(uint32_t *__restrict__ words) { words[threadIdx.x] = 0u; }
+
 }  // namespace
 
 extern "C" {
@@ -211,6 +249,28 @@ int accumulate_embedding_wgrad_timed(const void *ids, const void *grad, void *ma
     return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
                       grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
                       main_grad_dtype, workspace, workspace_bytes, stream, events);
+}
+
+int accumulate_embedding_wgrad_no_alloc(const void *ids, const void *grad, void *main_grad,
+                                        int64_t num_tokens, int64_t hidden,
+                                        int64_t num_embeddings, int64_t grad_row_stride,
+                                        int64_t main_grad_row_stride, int ids_dtype,
+                                        int grad_dtype, int main_grad_dtype, hipStream_t stream) {
+    int st = check_common(num_tokens, hidden, num_embeddings, ids_dtype, grad_dtype,
+                          main_grad_dtype);
+    if (st != EWG_OK) return st;
+    if (!ids || !grad || !main_grad) return EWG_INVALID_ARGUMENT;
+    if (grad_row_stride < hidden || main_grad_row_stride < hidden) return EWG_INVALID_ARGUMENT;
+    if (ws_layout(num_tokens, hidden).total > (size_t)EWG_NO_ALLOC_SCRATCH_BYTES)
+        return EWG_SCRATCH_TOO_SMALL;
+    void *ws = scratch_address();
+    if (!ws) return EWG_HIP_ERROR;
+    (void)hipGetLastError();
+    clear_header_kernel<<<1, kHeaderWords, 0, stream>>>(static_cast<uint32_t *>(ws));
+    if (hipGetLastError() != hipSuccess) return EWG_HIP_ERROR;
+    return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
+                      grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
+                      main_grad_dtype, ws, (size_t)EWG_NO_ALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int can_accumulate_embedding_wgrad_vocab_shard(int64_t num_tokens, int64_t hidden,
@@ -326,6 +386,7 @@ const char *ewg_status_string(int status) {
         case EWG_INVALID_ARGUMENT: return "invalid argument (null pointer, stride below hidden, unknown dtype code or misaligned workspace)";
         case EWG_WORKSPACE_TOO_SMALL: return "workspace smaller than accumulate_embedding_wgrad_workspace_bytes()";
         case EWG_HIP_ERROR: return "HIP error while enqueueing a kernel";
+        case EWG_SCRATCH_TOO_SMALL: return "sizes need more workspace than the library's static scratch (EWG_NO_ALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -299,3 +299,21 @@ def test_library_reads_no_environment_variable():
     out = subprocess.run(["nm", "-D", "--undefined-only", B.LIBRARY], capture_output=True,
                          text=True, check=True).stdout
     assert not re.search(r"\bgetenv\b", out), "libembedding_wgrad.so calls getenv"
+
+
+def test_no_alloc_entry_point_checks_sizes_before_any_device_call():
+    """accumulate_embedding_wgrad_no_alloc rejects sizes beyond its static scratch
+    (EWG_SCRATCH_TOO_SMALL) and sizes outside the envelope before it touches a device,
+    so these run without a GPU (the pointers are never dereferenced)."""
+    f = B.lib.accumulate_embedding_wgrad_no_alloc
+    n = 8192
+    ok = max(h for h in (11008, 7168) if B.workspace_bytes(n, h) <= B.NO_ALLOC_SCRATCH_BYTES)
+    assert ok == 11008
+    too_big = f(8, 8, 8, n, ok + 1, 129280, ok + 1, ok + 1, B.EWG_INT32, B.EWG_BF16,
+                B.EWG_FP32, None)
+    assert too_big == B.EWG_SCRATCH_TOO_SMALL
+    assert f(8, 8, 8, 3072, 128, 512, 128, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
+             None) == B.EWG_UNSUPPORTED
+    assert f(None, 8, 8, n, 128, 512, 128, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
+             None) == B.EWG_INVALID_ARGUMENT
+    assert "static scratch" in B.lib.ewg_status_string(B.EWG_SCRATCH_TOO_SMALL).decode()
