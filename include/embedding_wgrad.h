@@ -100,16 +100,14 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
 /*
  * Bytes of device workspace accumulate_embedding_wgrad and
  * accumulate_embedding_wgrad_sort_tokens need for these sizes (host only).
- * The workspace holds the chunk records and the fp32 partial sums of runs
- * longer than EWG_NROWS rows, and the counters the kernel's workgroups share;
- * its content between calls is not part of the interface except for three
- * int32 words: the first 4 bytes (see below); the one at byte offset
+ * The workspace holds the records of the runs longer than EWG_NROWS rows
+ * (positions and rows of their chunks) and the flag and counters the
+ * kernel's workgroups share: about 61 KB for 8192 tokens, whatever hidden is.
+ * Its content between calls is not part of the interface except for two
+ * int32 words: the first 4 bytes (see below), and the one at byte offset
  * EWG_WS_WAIT_TIMEOUTS_OFFSET, which counts the bounded waits inside the
- * kernel that gave up since the workspace was zero-filled; and the one at
- * EWG_WS_STOLEN_SHARES_OFFSET, the number of shares of long-run work that the
- * last call's waiting workgroups took over from workgroups that had not
- * started (a diagnostic: 0 when all of the launch's workgroups run together,
- * and the result is the same either way).
+ * kernel that gave up (and the long-run records found not to belong to the
+ * call) since the workspace was zero-filled.
  *
  * A wait that gives up is an ERROR of the call, not a diagnostic: the work
  * behind it was skipped and that call's main_grad is wrong. Every wait is
@@ -120,7 +118,6 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
  * 0 if the sizes are out of range.
  */
 #define EWG_WS_WAIT_TIMEOUTS_OFFSET 144
-#define EWG_WS_STOLEN_SHARES_OFFSET 148
 
 size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);
 
@@ -151,14 +148,13 @@ size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hi
  * 1024-thread workgroup per compute unit. Workgroup 0 sorts the keys in LDS
  * and publishes the chunks of runs longer than EWG_NROWS rows; meanwhile the
  * other workgroups finish every run of at most EWG_NROWS rows; then all of
- * them sum the chunks of the long runs and add those sums in chunk order.
- * Workgroups hand work to each other through the workspace, and every wait in
- * the kernel is bounded. A workgroup that waits long for long-run work of
- * workgroups that have not started (other work holding compute units) takes
- * that work over, so the call needs no particular number of workgroups
- * running at once. A wait that gives up is counted in the workspace's int32
- * at EWG_WS_WAIT_TIMEOUTS_OFFSET and its work is skipped. Any alignment is
- * accepted; 16-byte aligned rows take the vector path.
+ * them take column blocks of the long runs from a shared ticket, each block
+ * summed, folded in chunk order and finished inside one workgroup. The only
+ * wait between workgroups is for workgroup 0's flag, and workgroup 0 waits
+ * for nothing, so the call needs no particular number of workgroups running
+ * at once. The wait is bounded; one that gives up is counted in the
+ * workspace's int32 at EWG_WS_WAIT_TIMEOUTS_OFFSET and its work is skipped.
+ * Any alignment is accepted; 16-byte aligned rows take the vector path.
  *
  * The workspace carries counters from one call to the next: a call that did
  * not run to completion (for example a device fault) leaves it unusable
@@ -185,12 +181,13 @@ int accumulate_embedding_wgrad(const void *ids, const void *grad, void *main_gra
  * there: calls that overlap on one device (on different streams, or from
  * different threads without ordering) race and give wrong results. Sizes
  * whose workspace (accumulate_embedding_wgrad_workspace_bytes) exceeds
- * EWG_NO_ALLOC_SCRATCH_BYTES return EWG_SCRATCH_TOO_SMALL before anything is
- * enqueued; 64 MiB holds 8192 tokens up to hidden 11008. A bounded wait that
- * gives up is not reported by this entry point (use accumulate_embedding_wgrad
- * with a workspace to read the count).
+ * EWG_NO_ALLOC_SCRATCH_BYTES would return EWG_SCRATCH_TOO_SMALL before
+ * anything is enqueued; 256 KiB holds every size of the envelope (about 61 KB
+ * for 8192 tokens, whatever hidden is), so that check is a guard. A bounded
+ * wait that gives up is not reported by this entry point (use
+ * accumulate_embedding_wgrad with a workspace to read the count).
  */
-#define EWG_NO_ALLOC_SCRATCH_BYTES (64 << 20)
+#define EWG_NO_ALLOC_SCRATCH_BYTES (256 << 10)
 int accumulate_embedding_wgrad_no_alloc(const void *ids, const void *grad, void *main_grad,
                                         int64_t num_tokens, int64_t hidden,
                                         int64_t num_embeddings, int64_t grad_row_stride,

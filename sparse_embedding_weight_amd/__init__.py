@@ -30,7 +30,6 @@ from ._binding import (  # noqa: F401
     position_bits,
     raise_if_waits_gave_up,
     sort_tokens,
-    stolen_shares,
     wait_timeouts,
     workspace_bytes,
 )

@@ -29,7 +29,7 @@ MANY_MAX_EMBEDDINGS = 262144      # EWG_MANY_MAX_EMBEDDINGS
 EWG_INT32, EWG_INT64, EWG_BF16, EWG_FP32 = 0, 1, 2, 3
 (EWG_OK, EWG_UNSUPPORTED, EWG_INVALID_ARGUMENT, EWG_WORKSPACE_TOO_SMALL, EWG_HIP_ERROR,
  EWG_SCRATCH_TOO_SMALL) = range(6)
-NO_ALLOC_SCRATCH_BYTES = 64 << 20  # EWG_NO_ALLOC_SCRATCH_BYTES
+NO_ALLOC_SCRATCH_BYTES = 256 << 10  # EWG_NO_ALLOC_SCRATCH_BYTES
 
 DTYPE_CODE = {torch.int32: EWG_INT32, torch.int64: EWG_INT64,
               torch.bfloat16: EWG_BF16, torch.float32: EWG_FP32}
@@ -242,11 +242,11 @@ def accumulate_embedding_wgrad_no_alloc(ids: torch.Tensor, grad: torch.Tensor,
 
 
 def accumulate_with_grid_for_tests(ids: torch.Tensor, grad: torch.Tensor, main_grad: torch.Tensor,
-                              workspace: torch.Tensor, grid: int,
-                              defer_odd_shares: bool = False) -> None:
+                                   workspace: torch.Tensor, grid: int,
+                                   odd_skip_long: bool = False) -> None:
     """Tests only (include/embedding_wgrad_test.h): accumulate_embedding_wgrad launched
-    with `grid` workgroups; with defer_odd_shares every odd workgroup leaves its long
-    share to the combine tasks. Same result as accumulate_embedding_wgrad."""
+    with `grid` workgroups; with odd_skip_long the odd-numbered workgroups take no
+    column block of a long run. Same result as accumulate_embedding_wgrad."""
     if not can_accumulate_embedding_wgrad(ids, grad, main_grad):
         raise ValueError("accumulate_with_grid_for_tests: unsupported inputs")
     n, hidden = ids.numel(), grad.shape[-1]
@@ -257,7 +257,7 @@ def accumulate_with_grid_for_tests(ids: torch.Tensor, grad: torch.Tensor, main_g
             ids_flat.data_ptr(), grad2.data_ptr(), main_grad.data_ptr(), n, hidden,
             main_grad.shape[0], grad2.stride(0), main_grad.stride(0), DTYPE_CODE[ids.dtype],
             DTYPE_CODE[grad.dtype], DTYPE_CODE[main_grad.dtype], ws.data_ptr(), ws.numel(),
-            int(grid), 1 if defer_odd_shares else 0, _stream_handle(main_grad.device))
+            int(grid), 1 if odd_skip_long else 0, _stream_handle(main_grad.device))
     if st != EWG_OK:
         raise EmbeddingWgradError(st, "ewg_test_accumulate_embedding_wgrad")
 
@@ -407,14 +407,6 @@ def invalid_id_count(workspace: torch.Tensor) -> int:
 
 
 WS_WAIT_TIMEOUTS_OFFSET = 144   # EWG_WS_WAIT_TIMEOUTS_OFFSET
-WS_STOLEN_SHARES_OFFSET = 148   # EWG_WS_STOLEN_SHARES_OFFSET
-
-
-def stolen_shares(workspace: torch.Tensor) -> int:
-    """Shares of long-run work that the last call's waiting workgroups took over
-    from workgroups that had not started (diagnostic word; synchronises)."""
-    o = WS_STOLEN_SHARES_OFFSET
-    return int(workspace[o:o + 4].view(torch.int32).item())
 
 
 def wait_timeouts(workspace: torch.Tensor) -> int:

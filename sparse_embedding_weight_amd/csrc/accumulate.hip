@@ -1,6 +1,6 @@
-// The whole accumulation in one kernel: sort, chunk sums, single-chunk runs
-// finished in place, and the ordered combine of long runs. One 1024-thread
-// workgroup per compute unit (at least two workgroups).
+// The whole accumulation in one kernel: sort, chunk sums, runs of at most 10
+// rows finished in place, and long runs finished by column blocks. One
+// 1024-thread workgroup per compute unit (at least two workgroups).
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
 // introduction's two bullets (sort the ids with their positions, sum each
@@ -14,44 +14,35 @@
 //   1. Workgroup 0 (dispatched first, it never waits for anyone) radix-sorts
 //      the packed keys in LDS (sort_lds.h) and writes, with device-coherent
 //      stores, one record per chunk of a run longer than 10 rows (its row
-//      positions and run), one per such run (main_grad row, first chunk, chunk
-//      count, first combine task). Once every store has completed it sets
-//      the ready flag to the call's epoch (a nonzero number per call).
+//      positions and run) and one per such run (main_grad row, first chunk,
+//      chunk count, width of its column blocks, first block). Once every
+//      store has completed it sets the ready flag to the call's epoch (a
+//      nonzero number per call); the number of blocks comes with the flag.
 //   2. Meanwhile every other workgroup builds an LDS hash table of the ids
 //      and finishes its equal-cost share of the runs of at most 10 rows (a run
 //      of at most 10 rows is one chunk: it needs its rows in position order,
 //      not a global sort).
-//   3. The first wave of a workgroup to be done with its short runs waits
-//      for the flag, claims the workgroup's fixed share of the (long chunk,
-//      column tile) units and stages its records in LDS; every wave takes
-//      units as soon as it is done with its short runs and that is staged
-//      (no barrier in between), stores their fp32 chunk sums in the partial
-//      buffer with device-coherent stores and, once all have completed, the
-//      workgroup adds its count of each run's units to that run's counter for
-//      its group of workgroups.
-//   4. Then whole workgroups take combine tasks (one long run, one block of
-//      columns) from a ticket counter: wait until the run's units are all
-//      counted, stage its chunk sums in LDS, add them in chunk order from +0,
-//      round, add to main_grad, round.
-//   5. The last workgroup to finish clears the ticket, the exit counters and
-//      the flag for the next call. (These live in the workspace header, whose
-//      place does not depend on the sizes of a call; the per-run counters do,
-//      so workgroup 0 zeroes them before it raises the flag.)
-// Device-scope atomics on one address are serialised, and a wave's atomic
-// that returns a value also holds back its later loads (the vector memory
-// counter drains in order), so the kernel claims fine-grained work through
-// LDS counters and touches every shared counter about once per workgroup.
-// The flag is raised by workgroup 0, which waits for nothing before it; a
-// combine task waits only for the long units of the shares of other
-// workgroups, which wait for nothing but the flag. If such a wait lasts long
-// (200 us: some workgroups of the launch have not started, because more were
-// launched than fit or other work holds compute units), the waiting workgroup
-// claims the run's unclaimed shares and sums them itself, so every wait ends
-// whatever number of workgroups runs at once. Every wait is bounded; a wait
-// that gives up is counted in the workspace header and its work skipped.
+//   3. Then every workgroup takes column blocks of long runs from a device-
+//      wide ticket until none is left. A block is one long run over a range of
+//      columns. Each workgroup first stages the positions of every long chunk
+//      in LDS (once per call); for a block its waves sum every chunk of the
+//      block (fp32, from +0, rows in position order) into LDS; then each
+//      column adds its chunk sums in chunk order from +0, rounds once and is
+//      added to main_grad. The chunk sums never leave the compute unit, and no
+//      workgroup waits for another except for the flag. A run's blocks are as
+//      wide as its chunk sums fit in LDS and its grad bytes fit about one
+//      round of loads of the workgroup (one 10-row item in flight per wave),
+//      so a deep run is spread over many workgroups and a shallow one covers
+//      up to 2048 columns.
+//   4. The last workgroup to finish clears the ticket, the exit counters and
+//      the flag for the next call (they live in the workspace header).
+// The flag is raised by workgroup 0, which waits for nothing before it, so the
+// one wait of the kernel ends whatever number of workgroups runs at once. It
+// is bounded all the same; a wait that gives up is counted in the workspace
+// header and its work skipped.
 //
-// A column tile is 64 lanes x VEC columns (8 for bf16 grad, 4 for fp32), laid
-// out in lane-contiguous pieces (piece_cols in ewg_device.h).
+// A column tile of the short runs is 64 lanes x VEC columns (8 for bf16 grad,
+// 4 for fp32), laid out in lane-contiguous pieces (piece_cols in ewg_device.h).
 #include <hip/hip_ext.h>
 
 #include "chunk_sums.h"
@@ -63,14 +54,23 @@ namespace ewg {
 namespace {
 
 constexpr int64_t kWaitLimit = 1 << 22;  // polls before a wait gives up (seconds)
-constexpr uint64_t kStealAfterTicks = 20000;   // 200 us of the 100 MHz clock: a combine task
-                                               // then takes the run's unclaimed long shares
 constexpr int kHashSlots = 16384;        // > 2 x kMaxTokens: linear probing always ends
 constexpr int kHashBits = 14;
 constexpr int kOwnedMax = 256;           // short runs gathered per round by one follower
 constexpr uint32_t kNoSlot = 0xffffu;    // slot of a position whose id is left out
 constexpr int kMaxLongRuns = kMaxTokens / 11;
 constexpr int kMaxLongChunks = 2 * kMaxTokens / 11;
+constexpr int kMaxRunChunks = (kMaxTokens + kNRows - 1) / kNRows;   // chunks of the longest run
+constexpr int kBlockStageFloats = 26624; // chunk sums of one column block (104 KiB of LDS)
+constexpr int kMinBlockLog = 4;          // narrowest column block: 16 columns (64 bytes of fp32)
+constexpr int kMaxBlockLog = 11;         // widest column block: 2048 columns
+constexpr int kFoldCols = (1 << kMaxBlockLog) / kSortThreads;   // fold columns per thread
+constexpr int kLongItems = 1;           // items of a column block a wave has in flight at once
+// grad bytes of a column block: kLongItems items of 10 rows x 64 lanes x 16 bytes
+// for each of the 16 waves, so that a block is about one round of loads
+constexpr uint64_t kBlockBytes = (uint64_t)kLongItems * 16 * kNRows * 64 * 16;
+static_assert((kMaxRunChunks << kMinBlockLog) <= kBlockStageFloats,
+              "the narrowest block of the longest run fits the stage");
 
 struct FollowerSmem {
     uint32_t key[kHashSlots];               // (id + 1) | first position << (32 - position bits); 0 = empty
@@ -88,29 +88,17 @@ struct FollowerSmem {
     uint32_t next_unit;    // next (run, tile group) unit of the round to claim
 };
 
-struct CombineSmem {
-    float stage[kStageFloats];              // chunk sums of one task, [chunk][column]
-    u32x4 runs[kMaxLongRuns + 1];           // run records: row, first chunk, chunks, first task
+struct BlockSmem {
+    float stage[kBlockStageFloats];          // chunk sums of one block, [chunk][column]
+    u32x4 runs[kMaxLongRuns + 1];            // run records
+    uint16_t pos[kMaxLongChunks * kNRows];   // positions of every long chunk, kNRows each
+    uint8_t rows[kMaxLongChunks];            // rows of every long chunk
 };
-
-struct LongSmem {
-    u32x4 rec[2 * kMaxLongChunks];      // unit records of this workgroup's chunks, two halves each
-    uint32_t run_cnt[kMaxLongRuns];     // units of each long run this workgroup has finished
-    uint32_t claim;                     // next unit of this workgroup's share to claim
-};
-// A wave may stage a long share while its siblings still take short-run units
-// of their last round, which read only the run tables after the hash table:
-// the long share's LDS must lie inside the (then unused) hash keys.
-static_assert(sizeof(LongSmem) <= sizeof(uint32_t) * kHashSlots, "long share overlaps live LDS");
-// a take-over between two combine tasks keeps the run records staged for them
-static_assert(sizeof(LongSmem) <= offsetof(CombineSmem, runs), "long share overlaps the run records");
-static_assert(offsetof(FollowerSmem, key) == 0, "hash keys first");
 
 union AccSmem {
     SortSmem sort;
     FollowerSmem fol;
-    LongSmem lng;
-    CombineSmem comb;
+    BlockSmem blk;
 };
 
 __device__ __forceinline__ uint32_t hash_home(uint32_t id) {
@@ -341,6 +329,23 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 }
 
 
+// log2 of the column-block width of a long run of `chunks` chunks: the widest
+// power of two up to 2048 columns (no wider than hidden needs) whose chunk
+// sums fit the LDS stage and whose grad bytes (at most 10 rows per chunk) stay
+// within `target`, but no narrower than 64 bytes of a grad row (32 bf16 or 16
+// fp32 columns).
+__device__ __forceinline__ int block_log_width(uint32_t chunks, int hidden, uint64_t target,
+                                               int grad_bytes) {
+    const int min_lw = grad_bytes >= 4 ? kMinBlockLog : kMinBlockLog + 1;
+    int lw = min_lw;
+    while (lw < kMaxBlockLog && (1 << lw) < hidden) ++lw;
+    const uint64_t row_bytes = (uint64_t)chunks * kNRows * (uint64_t)grad_bytes;
+    while (lw > min_lw &&
+           (((uint64_t)chunks << lw) > (uint64_t)kBlockStageFloats || (row_bytes << lw) > target))
+        --lw;
+    return lw;
+}
+
 // ---- phase 1: the sorting workgroup -------------------------------------------
 
 constexpr int kQuickCheckKeys = kMaxTokens / 4;   // kept positions the quick check takes
@@ -378,20 +383,20 @@ __device__ __forceinline__ bool kept_id_exceeds_rows(SortSmem &ss, int pos_bits)
     return ss.long_seen != 0;
 }
 
-// Sort, mark runs, write the unit and run records, zero the runs' unit counts
-// and the tickets, publish the counts and raise the flag. With an id out of
+// Sort, mark runs, write the unit and run records (with the width of each
+// run's column blocks), zero the block ticket, publish the counts and raise
+// the flag. With an id out of
 // range there is nothing to do: all counts are 0.
 template <typename IdT>
 __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restrict__ ids, int n,
                                                int num_embeddings, int64_t id_base,
                                                bool skip_outside, int pos_bits, int id_bits,
-                                               int hidden, WsHeader *__restrict__ hdr,
+                                               int hidden, int grad_bytes,
+                                               WsHeader *__restrict__ hdr,
                                                __amdgpu_buffer_rsrc_t units_rs,
-                                               __amdgpu_buffer_rsrc_t runs_rs,
-                                               uint32_t *__restrict__ done,
-                                               uint32_t *__restrict__ shares, uint32_t epoch) {
+                                               __amdgpu_buffer_rsrc_t runs_rs, uint32_t epoch) {
     const int tid = threadIdx.x;
-    uint32_t n_lc = 0, n_lr = 0, n_tasks = 0;
+    uint32_t n_lc = 0, n_lr = 0, n_blocks = 0;
     const SortOutputs out0 = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
                               nullptr, nullptr};
     const int bad = load_keys<IdT>(ss, ids, n, num_embeddings, pos_bits, id_base, skip_outside);
@@ -446,31 +451,27 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
             store_coherent16(units_rs, (uint32_t)c * kUnitRecordBytes, u32x4{w[0], w[1], w[2], w[3]});
             store_coherent16(units_rs, (uint32_t)c * kUnitRecordBytes + 16, u32x4{w[4], w[5], w[6], w[7]});
         }
-        // run records, with the exclusive prefix of their combine tasks; unit counts to 0
-        uint32_t tasks = 0, chunks = 0;
+        // run records: chunk count and block width, and the exclusive prefix of
+        // the runs' column blocks (a block reads at most kBlockBytes of grad)
+        uint32_t blocks = 0, code = 0;
         if (tid < (int)n_lr) {
-            chunks = lr[4 * tid + 2];
-            const uint32_t wdt = (uint32_t)combine_width((int)chunks, hidden);
-            tasks = ((uint32_t)hidden + wdt - 1) / wdt;
+            const uint32_t chunks = lr[4 * tid + 2];
+            const int lw = block_log_width(chunks, hidden, kBlockBytes, grad_bytes);
+            blocks = (uint32_t)(((int64_t)hidden + (1 << lw) - 1) >> lw);
+            code = chunks | (uint32_t)lw << 16;
         }
         uint64_t total;
-        const uint32_t first_task = (uint32_t)block_exclusive_scan(tasks, ss.scan, &total);
+        const uint32_t first_block = (uint32_t)block_exclusive_scan(blocks, ss.scan, &total);
         if (tid < (int)n_lr)
             store_coherent16(runs_rs, (uint32_t)tid * kRunRecordBytes,
-                             u32x4{lr[4 * tid], lr[4 * tid + 1], chunks, first_task});
-        for (int i = tid; i < (int)n_lr * kDoneGroups; i += kSortThreads)
-            store_coherent(&done[(size_t)i * kDoneStride], 0u);
-        n_tasks = (uint32_t)total;
-
+                             u32x4{lr[4 * tid], lr[4 * tid + 1], code, first_block});
+        n_blocks = (uint32_t)total;
     }
-    // every share of long units unclaimed (they are claimed only after the flag)
-    for (int i = tid; i < (int)gridDim.x; i += kSortThreads) store_coherent(&shares[(size_t)i * kDoneStride], 0u);
     if (tid == 0) {
         store_coherent(&hdr->pub_long_chunks, n_lc);
         store_coherent(&hdr->pub_long_runs, n_lr);
-        store_coherent(&hdr->pub_tasks, n_tasks);
-        store_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 0u);
-        store_coherent(&hdr->task_ticket, 0u);
+        store_coherent(&hdr->pub_blocks, n_blocks);
+        store_coherent(&hdr->block_ticket, 0u);
     }
     // every store of every wave has completed, then the flag goes up
     __builtin_amdgcn_s_waitcnt(0);
@@ -478,16 +479,15 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
     if (tid == 0) store_coherent(&hdr->ready, epoch);
 }
 
-// ---- phase 3: chunks of long runs ---------------------------------------------
+// ---- phase 3: column blocks of long runs ----------------------------------------
 
-// Wave-level wait for this call's flag; false if the wait gave up. The flag
-// and the published counts (combine tasks, long chunks, long runs) are read by
+// and the published counts (column blocks, long chunks, long runs) are read by
 // one 16-byte load: the counts had completed before the flag was stored, so
 // the load that sees the flag returns them too.
 __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint32_t epoch,
-                                                uint32_t *n_tasks, uint32_t *n_lc, uint32_t *n_lr) {
+                                                uint32_t *n_blocks, uint32_t *n_lc, uint32_t *n_lr) {
     static_assert(offsetof(WsHeader, ready) % 16 == 0 &&
-                      offsetof(WsHeader, pub_tasks) == offsetof(WsHeader, ready) + 4 &&
+                      offsetof(WsHeader, pub_blocks) == offsetof(WsHeader, ready) + 4 &&
                       offsetof(WsHeader, pub_long_chunks) == offsetof(WsHeader, ready) + 8 &&
                       offsetof(WsHeader, pub_long_runs) == offsetof(WsHeader, ready) + 12,
                   "flag and counts in one 16-byte word");
@@ -496,7 +496,7 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     for (;;) {
         const u32x4 v = load_coherent16(h, (uint32_t)offsetof(WsHeader, ready));
         if ((uint32_t)__builtin_amdgcn_readfirstlane(v.x) == epoch) {
-            *n_tasks = __builtin_amdgcn_readfirstlane(v.y);
+            *n_blocks = __builtin_amdgcn_readfirstlane(v.y);
             *n_lc = __builtin_amdgcn_readfirstlane(v.z);
             *n_lr = __builtin_amdgcn_readfirstlane(v.w);
             return true;
@@ -509,291 +509,201 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     }
 }
 
-// First long unit of share w of the launch's gridDim.x shares of `total`.
-__device__ __forceinline__ uint32_t share_begin(uint32_t total, uint32_t w) {
-    return (uint32_t)((uint64_t)total * w / gridDim.x);
-}
-
-// The share that holds unit u (< total).
-__device__ __forceinline__ uint32_t share_of(uint32_t total, uint32_t u) {
-    uint32_t w = (uint32_t)(((uint64_t)u * gridDim.x) / total);
-    while (w + 1 < gridDim.x && share_begin(total, w + 1) <= u) ++w;
-    while (w > 0 && share_begin(total, w) > u) --w;
-    return w;
-}
-
-// Share w's slot (128 bytes apart, zeroed by workgroup 0 before the flag) goes
-// from 0 to `mark` once: 1 when its own workgroup takes it, 2 when a waiting
-// combine task does. True if this call made that change.
-__device__ __forceinline__ bool claim_share(uint32_t *__restrict__ shares, uint32_t w, uint32_t mark) {
-    uint32_t expected = 0u;
-    return __hip_atomic_compare_exchange_strong(&shares[(size_t)w * kDoneStride], &expected, mark,
-                                                __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Words of the long-unit hand-off, outside the LDS union: kLongElect holds
-// the number of the last long_units call whose staging wave was elected;
-// kLongState = call number << 2 | kStateNoFlag | kStateNoShare, published by
-// the staging wave; kLongChunks / kLongRuns / kLongTasks the published counts.
-constexpr int kLongElect = 0, kLongState = 1, kLongChunks = 2, kLongRuns = 3, kLongTasks = 4;
-constexpr int kLongWords = 5;
-constexpr uint32_t kStateNoFlag = 1u, kStateNoShare = 2u;
-
-// Long units (chunk c, column tile k) = c * tiles + k. Workgroup w of W
-// takes units [w * U / W, (w + 1) * U / W) of the U = chunks * tiles units:
-// the shares are fixed by the published chunk count alone, so no device-wide
-// counter is touched while the units run (a device-scope atomic in a wave
-// also holds back that wave's next loads until it returns).
-//
-// The waves enter one by one (after their short runs, on the first call) and
-// the first to enter stages the share for all: on the first call it waits for
-// the flag and loads the published counts; it claims the share's slot (mark 1
-// for the workgroup's own share, 2 for a take-over, 0 to leave the share
-// alone), copies the records of the share's chunks to LDS while the claim is
-// in flight, and publishes the outcome in `s_long`. The other waves wait for
-// that on LDS, not at a barrier, so a wave that is done with its short runs
-// starts long units while its siblings still finish theirs. The waves then
-// claim units one at a time with an LDS counter; each unit's fp32 chunk sums
-// go to its partial row with device-coherent stores. The finished units are
-// counted per run in LDS and added to the run's counter of this workgroup's
-// group once, after all stores of the workgroup have completed. `call` is the
-// number of this call in the workgroup (1, 2, ...; the same in every wave).
+// One column block [col0, col0 + min(2^lw, hidden - col0)) of the long run
+// whose `chunks` chunks start at long chunk `first` (main_grad row `row`), by
+// all 1024 threads. Lanes take
+// (chunk, piece) pairs: a row of the block is 2^lw / VEC pieces of VEC
+// columns, a wave covers 64 of them, so several chunks when the block is
+// narrower than 64 pieces and one tile of 64 pieces of one chunk otherwise.
+// Each lane sums its chunk's rows in position order from +0 in fp32 and puts
+// the sums in LDS; after a barrier each column adds its chunk sums in chunk
+// order from +0, rounds once to grad's dtype and is added to main_grad (whose
+// old values were loaded with the first grad loads).
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ bool long_units(LongSmem &ls, uint32_t *s_long, uint32_t call,
-                                           bool first_call, uint32_t share, uint32_t mark,
-                                           uint32_t *__restrict__ shares, WsHeader *__restrict__ hdr,
-                                           __amdgpu_buffer_rsrc_t units_rs,
-                                           uint32_t *__restrict__ done, uint32_t n_lc_in,
-                                           uint32_t n_lr_in, uint32_t n_lc_max, uint32_t n_lr_max,
-                                           int n, const typename G::T *__restrict__ grad,
-                                           int64_t grad_stride, float *__restrict__ partial,
-                                           int64_t partial_stride, int hidden, int tiles,
-                                           uint32_t epoch) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int full_tiles = hidden / (64 * VEC);
-    // every branch below is on a wave-uniform value; the single-lane LDS
-    // updates are whole-wave atomics in which only lane 0 changes anything
-    const uint32_t one = lane == 0 ? 1u : 0u;
-    const uint32_t prev = call - 1u;
-    const bool stager = (uint32_t)__builtin_amdgcn_readfirstlane(
-                            atomicCAS(&s_long[kLongElect], prev, lane == 0 ? call : prev)) == prev;
-    if (stager) {
-        bool ok = true;
-        uint32_t lc = n_lc_in, lr = n_lr_in, nt = 0u;
-        if (first_call) {
-            ok = wave_wait_ready(hdr, epoch, &nt, &lc, &lr);
-            lc = min(lc, n_lc_max);
-            lr = min(lr, n_lr_max);
-            if (lane == 0) s_long[kLongTasks] = nt;
-        }
-        lc = __builtin_amdgcn_readfirstlane(lc);
-        lr = __builtin_amdgcn_readfirstlane(lr);
-        bool won = false;
-        if (ok && mark != 0u) {
-            const uint32_t total = lc * (uint32_t)tiles;
-            const uint32_t lo = share_begin(total, share), hi = share_begin(total, share + 1);
-            const uint32_t c_lo = lo / (uint32_t)tiles;
-            const uint32_t c_hi = hi > lo ? (hi - 1) / (uint32_t)tiles + 1 : c_lo;
-            // the claim is in flight together with the loads of the records
-            uint32_t w = 0u;
-            if (lane == 0) w = claim_share(shares, share, mark) ? 1u : 0u;
-            for (uint32_t i = (uint32_t)lane; i < 2 * (c_hi - c_lo); i += 64)
-                ls.rec[i] = load_coherent16(units_rs, (2 * c_lo + i) * 16u);
-            for (uint32_t r = (uint32_t)lane; r < lr; r += 64) ls.run_cnt[r] = 0u;
-            if (lane == 0) ls.claim = 0u;
-            won = __builtin_amdgcn_readfirstlane(w) != 0u;
-        }
-        if (lane == 0) {
-            s_long[kLongChunks] = lc;
-            s_long[kLongRuns] = lr;
-        }
-        const uint32_t state = call << 2 | (ok ? 0u : kStateNoFlag) | (won ? 0u : kStateNoShare);
-        // the records, counters and counts above are visible before the state
-        __hip_atomic_store(&s_long[kLongState], state, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    uint32_t state;
-    int64_t spins = 0;
-    for (;;) {
-        state = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(&s_long[kLongState], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if ((state >> 2) == call) break;
-        // the staging wave waits at most kWaitLimit polls of the flag and a few loads
-        if (++spins > 16 * kWaitLimit) {
-            if (lane == 0) fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-            state = call << 2 | kStateNoFlag;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-    if (state & (kStateNoFlag | kStateNoShare)) return false;   // uniform over the workgroup
-
-    const uint32_t n_lc = s_long[kLongChunks], n_lr = s_long[kLongRuns];
-    const uint32_t total = n_lc * (uint32_t)tiles;
-    const uint32_t lo = share_begin(total, share);
-    const uint32_t hi = share_begin(total, share + 1);
-    const uint32_t c_lo = lo / (uint32_t)tiles;
-    for (;;) {
-        const uint32_t u = lo + __builtin_amdgcn_readfirstlane(atomicAdd(&ls.claim, one));
-        if (u >= hi) break;
-        const uint32_t c = u / (uint32_t)tiles;
-        const int tile = (int)(u - c * (uint32_t)tiles);
-        const u32x4 ra = ls.rec[2 * (c - c_lo)], rb = ls.rec[2 * (c - c_lo) + 1];
-        uint32_t w[6] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y};
+__device__ __forceinline__ void long_block(BlockSmem &bs, int lw, uint32_t row, uint32_t first,
+                                           uint32_t chunks, int col0,
+                                           const typename G::T *__restrict__ grad,
+                                           int64_t grad_stride, typename M::T *__restrict__ main_grad,
+                                           int64_t mg_stride, int hidden) {
+    using GT = typename G::T;
+    using MT = typename M::T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int width = 1 << lw;
+    const int wc = hidden - col0 < width ? hidden - col0 : width;
+    MT *mrow = main_grad + (int64_t)row * mg_stride + col0;
+    MT old[kFoldCols];
 #pragma unroll
-        for (int q = 0; q < 6; ++q) w[q] = __builtin_amdgcn_readfirstlane(w[q]);
-        int rows = (int)(w[5] & 0xffffu);
-        rows = rows < 1 ? 1 : (rows > kNRows ? kNRows : rows);
-        int32_t pos[kNRows];
+    for (int i = 0; i < kFoldCols; ++i) {
+        const int j = tid + i * kSortThreads;
+        if (j < wc) old[i] = mrow[j];
+    }
+    constexpr int kVecLog = VEC == 8 ? 3 : (VEC == 4 ? 2 : (VEC == 2 ? 1 : 0));
+    static_assert((1 << kVecLog) == VEC, "VEC is 1, 2, 4 or 8");
+    const int plog = lw - kVecLog;                 // pieces per row, log2 (>= 2)
+    const int llog = plog < 6 ? plog : 6;          // lanes per row, log2
+    const int tlog = plog - llog;                  // tiles of 64 pieces per row, log2
+    const int per = 64 >> llog;                    // chunks per wave item
+    const int items = (((int)chunks + per - 1) / per) << tlog;
+    const int kl = lane >> llog;
+    const int pl = lane & ((1 << llog) - 1);
+    // kLongItems items per wave at a time: all their row loads are in flight
+    // before the first add
+    for (int it0 = wave; it0 < items; it0 += kLongItems * kSortWaves) {
+        int k[kLongItems], lc[kLongItems], rows[kLongItems];
+        bool whole[kLongItems], active[kLongItems];
+        const uint16_t *pp[kLongItems];
+        const GT *gcol[kLongItems];
 #pragma unroll
-        for (int r = 0; r < kNRows; ++r) {
-            const uint32_t q = (w[r >> 1] >> (16 * (r & 1))) & 0xffffu;
-            pos[r] = q < (uint32_t)n ? (int32_t)q : 0;   // every row inside grad
+        for (int q = 0; q < kLongItems; ++q) {
+            const int it = it0 + q * kSortWaves;
+            k[q] = (it >> tlog) * per + kl;
+            lc[q] = (((it & ((1 << tlog) - 1)) << 6) + pl) * VEC;   // column in the block
+            active[q] = it < items && k[q] < (int)chunks && lc[q] < wc;
+            whole[q] = active[q] && lc[q] + VEC <= wc;
+            rows[q] = active[q] ? (int)bs.rows[first + k[q]] : 0;
+            pp[q] = &bs.pos[(first + (active[q] ? k[q] : 0)) * kNRows];
+            gcol[q] = grad + col0 + lc[q];
         }
-        const uint32_t run = w[5] >> 16;
-        // a record of another call (never expected) is counted and its unit skipped
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(rb.w) == epoch && run < n_lr) {
-            chunk_tiles_any<G, M, VEC>(pos, rows, 0, (int)c, grad, grad_stride, nullptr, 0,
-                                       partial, partial_stride, hidden, tile, tile + 1,
-                                       full_tiles);
-            atomicAdd(&ls.run_cnt[run], one);
-        } else {
-            fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), one);
-        }
-    }
-    // the chunk sums of every wave have completed before they are counted
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const size_t grp = blockIdx.x % kDoneGroups;
-    for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads) {
-        const uint32_t m = ls.run_cnt[r];
-        if (m) fetch_add_coherent(&done[((size_t)r * kDoneGroups + grp) * kDoneStride], m);
-    }
-    return true;
-}
-
-// ---- phase 4: ordered combine of long runs -------------------------------------
-
-// Where a workgroup stands in its combine tasks between two calls of
-// combine_tasks (the values are the same in every thread).
-struct CombineCursor {
-    uint32_t task;        // the task being waited for, if have_task
-    bool have_task;
-    int64_t spins;        // polls spent on that task's wait
-    uint32_t n_lc, n_lr, n_tasks;   // the published counts, as the flag's load returned them
-    bool runs_loaded;     // the run records are in LDS (nothing else writes that part later)
-};
-
-// Returns false once no combine task is left. Returns true, with the task
-// kept in the cursor, when the current task's run still needs the shares
-// [*w_lo, *w_hi) that no workgroup has taken: the caller takes and processes
-// them (long_units, which reuses this LDS) and calls again to resume the task.
-template <typename G, typename M, int VEC>
-__device__ __forceinline__ bool combine_tasks(AccSmem &sm, uint32_t *s_word, CombineCursor &cur,
-                                              uint32_t *w_lo, uint32_t *w_hi,
-                                              WsHeader *__restrict__ hdr,
-                                              __amdgpu_buffer_rsrc_t runs_rs,
-                                              uint32_t *__restrict__ done, bool flag_seen,
-                                              float *__restrict__ partial,
-                                              int64_t partial_stride,
-                                              typename M::T *__restrict__ main_grad,
-                                              int64_t mg_stride, int hidden, int tiles,
-                                              int num_embeddings, uint32_t n_lc_max,
-                                              uint32_t n_lr_max) {
-    CombineSmem &cs = sm.comb;
-    const int tid = threadIdx.x;
-    // The counts are those the flag's load returned (without the flag, which
-    // never fails to come, there is no task to take). The run records are
-    // loaded once, before the first ticket (taking the ticket first and the
-    // records only with a task cost 2 us on small calls, no time on large).
-    if (!flag_seen) return false;
-    const int n_lr = (int)min(cur.n_lr, n_lr_max);
-    const uint32_t n_tasks = cur.n_tasks;
-    if (n_lr == 0 || n_tasks == 0) return false;   // uniform
-    const uint32_t n_lc = min(cur.n_lc, n_lc_max);
-    const uint32_t total = n_lc * (uint32_t)tiles;
-    if (!cur.runs_loaded) {   // uniform
-        for (int r = tid; r < n_lr; r += kSortThreads)
-            cs.runs[r] = load_coherent16(runs_rs, (uint32_t)r * kRunRecordBytes);
-        __syncthreads();
-        cur.runs_loaded = true;
-    }
-
-    for (;;) {
-        if (!cur.have_task) {   // uniform
-            if (tid == 0) {
-                // a cheap look first: most late workgroups find the tasks gone
-                // without a serialised atomic
-                uint32_t t = load_coherent(&hdr->task_ticket);
-                if (t < n_tasks) t = fetch_add_coherent(&hdr->task_ticket, 1u);
-                s_word[2] = t;
-            }
-            __syncthreads();
-            cur.task = s_word[2];
-            cur.have_task = true;
-            cur.spins = 0;
-        }
-        const uint32_t t = cur.task;
-        if (t >= n_tasks) return false;   // uniform
-        // the run: the last one whose first task is at or before t
-        int lo = 0, hi = n_lr;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (cs.runs[mid].w <= t) lo = mid; else hi = mid;
-        }
-        const u32x4 rec = cs.runs[lo];
-        const uint32_t row = rec.x, first = rec.y, chunks = rec.z;
-        const int wdt = combine_width((int)chunks, hidden);
-        const int64_t col0 = (int64_t)(t - rec.w) * wdt;
-        // a record that does not describe this call's work is skipped
-        const bool valid = rec.w <= t && row < (uint32_t)num_embeddings && chunks >= 1 &&
-                           first < n_lc_max && chunks <= n_lc_max - first && col0 < hidden;
-        // Wait until the run's units are all counted. If that takes long, some
-        // workgroups of the launch are not running (more were launched than fit,
-        // or other work holds compute units): then the caller processes the
-        // run's shares that nobody has taken yet, and the wait resumes.
-        // Stealing needs the run's units inside this call's unit list.
-        const bool can_steal = flag_seen && valid && first + chunks <= n_lc;
-        if (tid == 0) {
-            uint32_t status = valid ? 0u : 3u;   // 0 waiting, 1 done, 2 steal, 3 give up
-            const uint32_t target = chunks * (uint32_t)tiles;
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            int64_t spins = cur.spins;
-            while (status == 0u) {
-                uint32_t sum = 0;
-                for (int g = 0; g < kDoneGroups; ++g)
-                    sum += load_coherent(&done[((size_t)lo * kDoneGroups + g) * kDoneStride]);
-                if (sum >= target) {
-                    status = 1u;
-                } else if (++spins > kWaitLimit) {
-                    fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-                    status = 3u;
-                } else if (can_steal && __builtin_amdgcn_s_memrealtime() - t0 > kStealAfterTicks) {
-                    status = 2u;
-                } else {
-                    __builtin_amdgcn_s_sleep(2);
+        GT raw[kLongItems][kNRows][VEC];
+#pragma unroll
+        for (int q = 0; q < kLongItems; ++q)
+#pragma unroll
+            for (int r = 0; r < kNRows; ++r)
+                if (whole[q] && r < rows[q])
+                    load_vec<GT, VEC>(gcol[q] + (int64_t)pp[q][r] * grad_stride, raw[q][r]);
+#pragma unroll
+        for (int q = 0; q < kLongItems; ++q) {
+            if (whole[q]) {   // a whole piece
+                float acc[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < kNRows; ++r)
+                    if (r < rows[q]) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + G::widen(raw[q][r][e]);
+                    }
+                float *dst = &bs.stage[(k[q] << lw) + lc[q]];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
+            } else if (active[q]) {   // the ragged end of the row, element by element
+                for (int e = 0; e < VEC && lc[q] + e < wc; ++e) {
+                    float a = 0.0f;
+                    for (int r = 0; r < rows[q]; ++r)
+                        a = a + G::widen(gcol[q][(int64_t)pp[q][r] * grad_stride + e]);
+                    bs.stage[(k[q] << lw) + lc[q] + e] = a;
                 }
             }
-            s_word[3] = status;
-            s_word[0] = (uint32_t)(spins < kWaitLimit ? spins : kWaitLimit);   // free since the run list loaded
         }
-        __syncthreads();
-        const uint32_t status = s_word[3];
-        cur.spins = (int64_t)s_word[0];
-        if (status == 2u) {   // uniform
-            // the run's units are [first * tiles, (first + chunks) * tiles)
-            *w_lo = share_of(total, first * (uint32_t)tiles);
-            *w_hi = share_of(total, (first + chunks) * (uint32_t)tiles - 1u) + 1u;   // <= gridDim.x
-            __syncthreads();   // every thread has read s_word before the caller reuses it
-            return true;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kFoldCols; ++i) {
+        const int wave_j0 = (tid & ~63) + i * kSortThreads;
+        if (wave_j0 < wc) {   // uniform over the wave
+            const int j = tid + i * kSortThreads;
+            const float *col = &bs.stage[j < wc ? j : wave_j0];
+            float acc = 0.0f;
+            // the adds stay in chunk order; the LDS reads of a group of 8 are
+            // all issued before the first add
+            int k = 0;
+            for (; k + 8 <= (int)chunks; k += 8) {
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = col[(k + q) << lw];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc = acc + v[q];
+            }
+            for (; k < (int)chunks; ++k) acc = acc + col[k << lw];
+            if (j < wc) mrow[j] = finish<G, M>(acc, old[i]);
         }
-        const bool task_ok = status == 1u;
-        cur.have_task = false;
-        __syncthreads();
-        if (task_ok) {   // uniform
-            combine_block<G, M>(cs.stage, row, first, chunks, col0, wdt, partial, partial_stride,
-                                main_grad, mg_stride, hidden);
+    }
+    __syncthreads();
+}
+
+// Wait for the flag (wave 0); stage the run records and the positions and
+// rows of every long chunk in LDS (once: every block reads them from there);
+// then take column blocks from the device-wide ticket until none is left
+// (take = false: wait, take nothing). A record that does not describe this
+// call's work is counted in the header's wait-timeout word and the blocks
+// that would use it are skipped.
+template <typename G, typename M, int VEC>
+__device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
+                                            WsHeader *__restrict__ hdr,
+                                            __amdgpu_buffer_rsrc_t units_rs,
+                                            __amdgpu_buffer_rsrc_t runs_rs, uint32_t n_lc_max,
+                                            uint32_t n_lr_max, int n, int num_embeddings,
+                                            const typename G::T *__restrict__ grad,
+                                            int64_t grad_stride,
+                                            typename M::T *__restrict__ main_grad,
+                                            int64_t mg_stride, int hidden, uint32_t epoch,
+                                            bool take) {
+    const int tid = threadIdx.x;
+    if (tid < 64) {   // wave 0
+        uint32_t nb = 0u, lc = 0u, lr = 0u;
+        const bool ok = wave_wait_ready(hdr, epoch, &nb, &lc, &lr);
+        if (tid == 0) {
+            s_word[0] = ok ? nb : 0u;
+            s_word[1] = lc;
+            s_word[2] = lr;
+            s_word[3] = 0u;   // staging errors, below
         }
+    }
+    __syncthreads();
+    const uint32_t n_blocks = s_word[0];
+    const uint32_t n_lc = min(s_word[1], n_lc_max), n_lr = min(s_word[2], n_lr_max);
+    __syncthreads();   // every thread has read s_word before it is reused
+    if (!take || n_blocks == 0u || n_lr == 0u) return;   // uniform
+    for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads)
+        bs.runs[r] = load_coherent16(runs_rs, r * (uint32_t)kRunRecordBytes);
+    uint32_t bad = 0u;
+    for (uint32_t c = (uint32_t)tid; c < n_lc; c += kSortThreads) {
+        const u32x4 a = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes);
+        const u32x4 b = load_coherent16(units_rs, c * (uint32_t)kUnitRecordBytes + 16u);
+        const uint32_t w[5] = {a.x, a.y, a.z, a.w, b.x};
+        uint32_t rows = b.y & 0xffffu;
+        if (b.w != epoch || (b.y >> 16) >= n_lr || b.z != c || rows < 1u || rows > (uint32_t)kNRows)
+            bad = 1u;
+        rows = rows < 1u ? 1u : (rows > (uint32_t)kNRows ? (uint32_t)kNRows : rows);
+        bs.rows[c] = (uint8_t)rows;
+#pragma unroll
+        for (int i = 0; i < kNRows; ++i) {
+            const uint32_t q = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            bs.pos[c * kNRows + i] = (uint16_t)(q < (uint32_t)n ? q : 0u);   // every row inside grad
+        }
+    }
+    if (bad) atomicOr(&s_word[3], 1u);
+    if (tid == 0) s_word[0] = fetch_add_coherent(&hdr->block_ticket, 1u);
+    __syncthreads();
+    const bool staged_ok = s_word[3] == 0u;   // s_word[3] is not written again
+    for (;;) {
+        const uint32_t b = s_word[0];
+        __syncthreads();   // every thread has read the claim before the next one lands
+        if (b >= n_blocks) break;   // uniform
+        // the next claim travels while this block is processed
+        uint32_t next = 0u;
+        if (tid == 0) next = fetch_add_coherent(&hdr->block_ticket, 1u);
+        // the run of block b: the last run whose first block is at or before b
+        int lo = 0, hi = (int)n_lr;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (bs.runs[mid].w <= b) lo = mid; else hi = mid;
+        }
+        const u32x4 rec = bs.runs[lo];
+        const uint32_t row = rec.x, first = rec.y, chunks = rec.z & 0xffffu;
+        const int lw = (int)((rec.z >> 16) & 0xffu);
+        const bool shape_ok = rec.w <= b && lw >= kMinBlockLog && lw <= kMaxBlockLog &&
+                              chunks > 1u && chunks <= (uint32_t)kMaxRunChunks &&
+                              (chunks << lw) <= (uint32_t)kBlockStageFloats;
+        const int64_t col0 = shape_ok ? (int64_t)(b - rec.w) << lw : (int64_t)hidden;
+        const bool valid = staged_ok && shape_ok && row < (uint32_t)num_embeddings &&
+                           first < n_lc && chunks <= n_lc - first && col0 < hidden;
+        if (valid)   // uniform
+            long_block<G, M, VEC>(bs, lw, row, first, chunks, (int)col0, grad, grad_stride,
+                                  main_grad, mg_stride, hidden);
+        else if (tid == 0)
+            fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
+        if (tid == 0) s_word[0] = next;
         __syncthreads();
     }
 }
@@ -804,26 +714,19 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
     int pos_bits, int id_bits,
     const typename G::T *__restrict__ grad, int64_t grad_stride,
     typename M::T *__restrict__ main_grad, int64_t mg_stride, int hidden, int tiles,
-    WsHeader *__restrict__ hdr, uint8_t *__restrict__ units,
-    uint8_t *__restrict__ runs, uint32_t *__restrict__ done, uint32_t *__restrict__ shares,
-    float *__restrict__ partial, int64_t partial_stride, uint32_t epoch, int defer_odd_shares) {
+    WsHeader *__restrict__ hdr, uint8_t *__restrict__ units, uint8_t *__restrict__ runs,
+    uint32_t epoch, int odd_skip_long) {
     __shared__ AccSmem sm;
-    __shared__ uint32_t s_word[4];   // LDS broadcasts between phases
-    __shared__ uint32_t s_long[kLongWords];   // long-share hand-off (kLongElect ...)
+    __shared__ uint32_t s_word[4];   // LDS broadcasts
     const int tid = threadIdx.x;
     const uint32_t n_lc_max = (uint32_t)(2 * n / 11), n_lr_max = (uint32_t)(n / 11);
     const __amdgpu_buffer_rsrc_t units_rs = buffer_range(units, n_lc_max * (uint32_t)kUnitRecordBytes);
     const __amdgpu_buffer_rsrc_t runs_rs = buffer_range(runs, n_lr_max * (uint32_t)kRunRecordBytes);
-    if (tid == 0) {   // read after the barriers of either first phase
-        s_long[kLongElect] = 0u;
-        s_long[kLongState] = 0u;
-        s_long[kLongTasks] = 0u;
-    }
 
     if (blockIdx.x == 0) {
         leader_publish<IdT>(sm.sort, ids, n, num_embeddings, id_base, skip_outside != 0, pos_bits,
-                            id_bits, hidden, hdr,
-                            units_rs, runs_rs, done, shares, epoch);
+                            id_bits, hidden, (int)sizeof(typename G::T), hdr, units_rs, runs_rs,
+                            epoch);
     } else {
         // the waves leave this one by one, as their short-run units run out
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
@@ -831,47 +734,14 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
                                             main_grad, mg_stride, hidden, tiles,
                                             (int)blockIdx.x - 1, (int)gridDim.x - 1);
     }
-    // Phases 3 and 4: the workgroup's own share (claimed with mark 1, unless a
-    // waiting combine task took it already; a test setting leaves every other
-    // share to the combine tasks: mark 0), then combine tasks. A combine task
-    // that waits long hands back the shares [w, w_end) its run still needs,
-    // taken over here with mark 2 (one copy of the long-unit code serves both).
-    uint32_t w = blockIdx.x, w_end = blockIdx.x + 1u;
-    uint32_t mark = defer_odd_shares && (blockIdx.x & 1u) ? 0u : 1u;
-    uint32_t call = 0u;
-    bool flag_seen = false;
-    CombineCursor cur;
-    cur.have_task = false;
-    cur.task = 0u;
-    cur.spins = 0;
-    cur.n_lc = cur.n_lr = cur.n_tasks = 0u;
-    cur.runs_loaded = false;
-    for (;;) {
-        for (; w < w_end; ++w) {
-            ++call;
-            const bool took = long_units<G, M, VEC>(sm.lng, s_long, call, call == 1u, w, mark,
-                                                    shares, hdr, units_rs, done, cur.n_lc,
-                                                    cur.n_lr, n_lc_max, n_lr_max, n, grad,
-                                                    grad_stride, partial, partial_stride, hidden,
-                                                    tiles, epoch);
-            if (call == 1u) {   // the flag and the counts, as the staging wave saw them
-                flag_seen = (s_long[kLongState] & kStateNoFlag) == 0u;
-                cur.n_lc = s_long[kLongChunks];
-                cur.n_lr = s_long[kLongRuns];
-                cur.n_tasks = s_long[kLongTasks];
-            }
-            if (took && mark == 2u && tid == 0)
-                fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->stolen_shares), 1u);
-            __syncthreads();
-        }
-        if (!combine_tasks<G, M, VEC>(sm, s_word, cur, &w, &w_end, hdr, runs_rs, done, flag_seen,
-                                      partial, partial_stride, main_grad, mg_stride, hidden,
-                                      tiles, num_embeddings, n_lc_max, n_lr_max))
-            break;
-        mark = 2u;
-    }
+    __syncthreads();   // the LDS of phases 1 and 2 is free from here on
+    // phase 3 (a test setting keeps odd workgroups out of it)
+    const bool take = !(odd_skip_long && (blockIdx.x & 1u));
+    long_blocks<G, M, VEC>(sm.blk, s_word, hdr, units_rs, runs_rs, n_lc_max, n_lr_max, n,
+                           num_embeddings, grad, grad_stride, main_grad, mg_stride, hidden, epoch,
+                           take);
 
-    // ---- phase 5: the last workgroup out resets the call's shared state ----
+    // ---- phase 4: the last workgroup out resets the call's shared state ----
     // two levels of counters, so that no address takes more than ~32 atomics
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -886,7 +756,7 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
         if (last) {
             for (int g = 0; g < kExitGroups; ++g) store_coherent(&hdr->exit_group[g][0], 0u);
             store_coherent(&hdr->exit_top, 0u);
-            store_coherent(&hdr->task_ticket, 0u);
+            store_coherent(&hdr->block_ticket, 0u);
             store_coherent(&hdr->ready, 0u);
         }
     }
@@ -897,7 +767,7 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, i
                   int pos_bits, int id_bits,
                   const void *grad, int64_t grad_stride, void *main_grad, int64_t mg_stride,
                   int hidden, void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                  int defer_odd_shares, hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream) {
+                  int odd_skip_long, hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream) {
     char *ws = static_cast<char *>(workspace);
     const int tiles = (hidden + 64 * VEC - 1) / (64 * VEC);
     const int grid = num_cus < 2 ? 2 : (num_cus > kMaxGrid ? kMaxGrid : num_cus);
@@ -908,20 +778,16 @@ hipError_t launch(const void *ids, int n, int num_embeddings, int64_t id_base, i
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws);
     uint8_t *units = reinterpret_cast<uint8_t *>(ws + l.units);
     uint8_t *runs = reinterpret_cast<uint8_t *>(ws + l.runs);
-    uint32_t *done = reinterpret_cast<uint32_t *>(ws + l.done);
-    uint32_t *shares = reinterpret_cast<uint32_t *>(ws + l.shares);
-    float *partial = reinterpret_cast<float *>(ws + l.partial);
     if (kstart && kstop)   // events taken by the dispatch itself: the kernel's own duration
         hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kSortThreads), 0, stream, kstart, kstop, 0,
                               ids_t, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits,
                               grad_t, grad_stride, mg_t, mg_stride, hidden, tiles, hdr, units, runs,
-                              done, shares, partial, l.partial_stride, epoch, defer_odd_shares);
+                              epoch, odd_skip_long);
     else
         kernel<<<grid, kSortThreads, 0, stream>>>(ids_t, n, num_embeddings, id_base, skip_outside,
                                                   pos_bits, id_bits, grad_t, grad_stride, mg_t,
-                                                  mg_stride, hidden, tiles, hdr, units, runs, done,
-                                                  shares, partial, l.partial_stride, epoch,
-                                                  defer_odd_shares);
+                                                  mg_stride, hidden, tiles, hdr, units, runs, epoch,
+                                                  odd_skip_long);
     return hipGetLastError();
 }
 
@@ -931,12 +797,12 @@ hipError_t dispatch_types(bool grad_bf16, bool mg_bf16, bool vec, const void *id
                           int id_bits, const void *grad,
                           int64_t grad_stride, void *main_grad, int64_t mg_stride, int hidden,
                           void *workspace, const WsLayout &l, int num_cus, uint32_t epoch,
-                          int defer_odd_shares, hipEvent_t kstart, hipEvent_t kstop,
+                          int odd_skip_long, hipEvent_t kstart, hipEvent_t kstop,
                           hipStream_t stream) {
 #define EWG_ACC(G, M, V)                                                                        \
     launch<IdT, G, M, V>(ids, n, num_embeddings, id_base, skip_outside, pos_bits, id_bits, grad,   \
                          grad_stride, main_grad, mg_stride, hidden, workspace, l, num_cus, epoch, \
-                         defer_odd_shares, kstart, kstop, stream)
+                         odd_skip_long, kstart, kstop, stream)
     if (grad_bf16) {
         if (mg_bf16) return vec ? EWG_ACC(BF16, BF16, 8) : EWG_ACC(BF16, BF16, 1);
         return vec ? EWG_ACC(BF16, F32, 8) : EWG_ACC(BF16, F32, 1);
@@ -953,17 +819,17 @@ hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool 
                              bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
-                             int num_cus, uint32_t epoch, int defer_odd_shares,
+                             int num_cus, uint32_t epoch, int odd_skip_long,
                              hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream) {
     if (ids_int64)
         return dispatch_types<int64_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
                                        skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride,
                                        main_grad, mg_stride, hidden, workspace, l, num_cus, epoch,
-                                       defer_odd_shares, kstart, kstop, stream);
+                                       odd_skip_long, kstart, kstop, stream);
     return dispatch_types<int32_t>(grad_bf16, mg_bf16, vec, ids, n, num_embeddings, id_base,
                                    skip_outside ? 1 : 0, pos_bits, id_bits, grad, grad_stride,
                                    main_grad, mg_stride, hidden, workspace, l, num_cus, epoch,
-                                   defer_odd_shares, kstart, kstop, stream);
+                                   odd_skip_long, kstart, kstop, stream);
 }
 
 }  // namespace ewg

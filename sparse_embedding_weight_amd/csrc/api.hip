@@ -89,7 +89,7 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                int64_t hidden, int64_t num_embeddings, int64_t id_base, bool shard,
                int64_t grad_row_stride, int64_t main_grad_row_stride, int ids_dtype,
                int grad_dtype, int main_grad_dtype, void *workspace, size_t workspace_bytes,
-               hipStream_t stream, hipEvent_t *events, int grid = 0, int defer_odd_shares = 0) {
+               hipStream_t stream, hipEvent_t *events, int grid = 0, int odd_skip_long = 0) {
     int st = shard ? (!is_known_dtype(ids_dtype) || !is_known_dtype(grad_dtype) ||
                               !is_known_dtype(main_grad_dtype)
                           ? EWG_INVALID_ARGUMENT
@@ -125,7 +125,7 @@ int accumulate(const void *ids, const void *grad, void *main_grad, int64_t num_t
                                      (int)num_embeddings, id_base, shard, pos_bits, id_bits, grad,
                                      grad_row_stride,
                                      main_grad, main_grad_row_stride, (int)hidden, workspace, l,
-                                     grid > 0 ? grid : num_cus(), next_epoch(), defer_odd_shares,
+                                     grid > 0 ? grid : num_cus(), next_epoch(), odd_skip_long,
                                      events ? events[2] : nullptr, events ? events[3] : nullptr,
                                      stream));
     if (st != EWG_OK) return st;
@@ -369,14 +369,14 @@ int ewg_test_accumulate_embedding_wgrad(const void *ids, const void *grad, void 
                                         int64_t num_embeddings, int64_t grad_row_stride,
                                         int64_t main_grad_row_stride, int ids_dtype,
                                         int grad_dtype, int main_grad_dtype, void *workspace,
-                                        size_t workspace_bytes, int grid, int defer_odd_shares,
+                                        size_t workspace_bytes, int grid, int odd_skip_long,
                                         hipStream_t stream) {
-    if (grid < 2 || grid > kMaxGrid || (defer_odd_shares != 0 && defer_odd_shares != 1))
+    if (grid < 2 || grid > kMaxGrid || (odd_skip_long != 0 && odd_skip_long != 1))
         return EWG_INVALID_ARGUMENT;
     return accumulate(ids, grad, main_grad, num_tokens, hidden, num_embeddings, 0, false,
                       grad_row_stride, main_grad_row_stride, ids_dtype, grad_dtype,
                       main_grad_dtype, workspace, workspace_bytes, stream, nullptr, grid,
-                      defer_odd_shares);
+                      odd_skip_long);
 }
 
 const char *ewg_status_string(int status) {

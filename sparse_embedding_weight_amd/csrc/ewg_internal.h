@@ -38,14 +38,14 @@ struct WsHeader {
     // call's epoch (nonzero); the last workgroup to finish sets it back to 0
     // (ready and the three counts form one 16-byte word, read by one load)
     uint32_t ready;
-    uint32_t pub_tasks;       // combine tasks of this call
+    uint32_t pub_blocks;      // column blocks of long runs in this call
     uint32_t pub_long_chunks; // long chunks of this call
     uint32_t pub_long_runs;   // long runs of this call
-    int32_t wait_timeouts;    // bounded waits that gave up (never expected)
-    int32_t stolen_shares;    // long shares a waiting combine task took over in the last call
-    int32_t pad1[26];
-    // line 2: next combine task to hand out
-    uint32_t task_ticket;
+    int32_t wait_timeouts;    // bounded waits that gave up, and records that did not
+                              // belong to the call (never expected)
+    int32_t pad1[27];
+    // line 2: next column block of a long run to hand out
+    uint32_t block_ticket;
     int32_t pad2[31];
     // line 3: groups of workgroups that have finished
     uint32_t exit_top;
@@ -55,8 +55,6 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
 static_assert(offsetof(WsHeader, wait_timeouts) == EWG_WS_WAIT_TIMEOUTS_OFFSET,
-              "documented diagnostic word");
-static_assert(offsetof(WsHeader, stolen_shares) == EWG_WS_STOLEN_SHARES_OFFSET,
               "documented diagnostic word");
 
 // Optional outputs of the sort step (all null in the accumulate path).
@@ -78,33 +76,27 @@ constexpr int kMaxGrid = 4095;       // workgroups of one launch, at most
 // is written by a call before that call reads it.
 struct WsLayout {
     size_t units;            // 32-byte record per long chunk (positions, rows, run)
-    size_t runs;             // 16-byte record per long run (row, first chunk, chunks, tasks)
-    size_t done;             // per long run: finished units, kDoneGroups counters of 128 bytes
-    size_t shares;           // per workgroup of the launch: who processes its long share
-    size_t partial;          // float[max_long_chunks][partial_stride]
+    size_t runs;             // 16-byte record per long run (row, first chunk, chunks and
+                             // block width, first block)
     size_t total;
-    int64_t partial_stride;  // floats per partial row
     int64_t max_long_chunks; // a run of L > 10 rows has ceil(L/10) <= 2L/11 chunks
     int64_t max_long_runs;   // a long run has at least 11 rows
 };
 
 constexpr size_t kUnitRecordBytes = 32;
 constexpr size_t kRunRecordBytes = 16;
-constexpr size_t kDoneStride = 32;   // uint32 words between two unit counters (128 bytes)
-constexpr int kDoneGroups = 8;       // unit counters per long run: one per group of workgroups
 
+// The workspace holds the header and the records of the long runs only: the
+// chunk sums of a long run never leave the compute unit that folds them, so
+// its size does not depend on hidden (the argument stays for the interface).
 inline WsLayout ws_layout(int64_t num_tokens, int64_t hidden) {
+    (void)hidden;
     WsLayout l;
     l.max_long_chunks = 2 * num_tokens / 11;
     l.max_long_runs = num_tokens / 11;
     l.units = sizeof(WsHeader);
     l.runs = round_up(l.units + kUnitRecordBytes * (size_t)(l.max_long_chunks + 1), 256);
-    l.done = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
-    l.shares = round_up(l.done + 4 * kDoneStride * kDoneGroups * (size_t)(l.max_long_runs + 1), 256);
-    l.partial = round_up(l.shares + 4 * kDoneStride * (size_t)kMaxGrid, 256);
-    l.partial_stride = (int64_t)round_up((size_t)hidden, 64);
-    l.total = round_up(l.partial + sizeof(float) * (size_t)l.partial_stride *
-                                       (size_t)l.max_long_chunks, 256);
+    l.total = round_up(l.runs + kRunRecordBytes * (size_t)(l.max_long_runs + 1), 256);
     return l;
 }
 
@@ -171,8 +163,8 @@ hipError_t launch_sort_tokens(const void *ids, bool ids_int64, int n, int num_em
 // compute unit. grad_bf16 / mg_bf16 select the element types; vec selects
 // 16-byte rows. Row v of main_grad belongs to id id_base + v, for v below
 // num_embeddings; with skip_outside other ids are left out, else they are
-// invalid (the call then touches nothing and reports them). defer_odd_shares
-// (tests only) leaves the long shares of odd workgroups to the combine tasks.
+// invalid (the call then touches nothing and reports them). odd_skip_long
+// (tests only): odd-numbered workgroups take no column block of a long run.
 // Calls of kMaxTokens < n <= kManyMaxTokens tokens (any n >= 1 works): five
 // kernels (tile sort, ranks, chunk lists, chunk sums, ordered combine), same
 // arithmetic as launch_accumulate. Ids must lie in [0, num_embeddings) with
@@ -188,7 +180,7 @@ hipError_t launch_accumulate(bool ids_int64, bool grad_bf16, bool mg_bf16, bool 
                              bool skip_outside, int pos_bits, int id_bits,
                              const void *grad, int64_t grad_stride, void *main_grad,
                              int64_t mg_stride, int hidden, void *workspace, const WsLayout &l,
-                             int num_cus, uint32_t epoch, int defer_odd_shares,
+                             int num_cus, uint32_t epoch, int odd_skip_long,
                              hipEvent_t kstart, hipEvent_t kstop, hipStream_t stream);
 
 }  // namespace ewg

@@ -49,18 +49,21 @@ def test_binding_constants_match_the_header():
         "EWG_MIN_TOKENS": B.MIN_TOKENS, "EWG_MAX_TOKENS": B.MAX_TOKENS, "EWG_NROWS": B.NROWS,
         "EWG_MANY_MAX_TOKENS": B.MANY_MAX_TOKENS, "EWG_MANY_MAX_EMBEDDINGS": B.MANY_MAX_EMBEDDINGS,
         "EWG_WS_WAIT_TIMEOUTS_OFFSET": B.WS_WAIT_TIMEOUTS_OFFSET,
-        "EWG_WS_STOLEN_SHARES_OFFSET": B.WS_STOLEN_SHARES_OFFSET,
         "EWG_INT32": B.EWG_INT32, "EWG_INT64": B.EWG_INT64, "EWG_BF16": B.EWG_BF16,
         "EWG_FP32": B.EWG_FP32, "EWG_OK": B.EWG_OK, "EWG_UNSUPPORTED": B.EWG_UNSUPPORTED,
         "EWG_INVALID_ARGUMENT": B.EWG_INVALID_ARGUMENT,
         "EWG_WORKSPACE_TOO_SMALL": B.EWG_WORKSPACE_TOO_SMALL, "EWG_HIP_ERROR": B.EWG_HIP_ERROR,
+        "EWG_SCRATCH_TOO_SMALL": B.EWG_SCRATCH_TOO_SMALL,
     }
     assert set(expected) <= set(c), sorted(set(expected) - set(c))
     for k, v in expected.items():
         assert c[k] == v, f"{k}: header {c[k]}, binding {v}"
-    # the two diagnostic words lie in the workspace header, 4-byte aligned, apart
-    assert c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] % 4 == 0 and c["EWG_WS_STOLEN_SHARES_OFFSET"] % 4 == 0
-    assert c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] != c["EWG_WS_STOLEN_SHARES_OFFSET"]
+    # the diagnostic word lies in the workspace header, 4-byte aligned, past the
+    # invalid-id count
+    assert c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] % 4 == 0 and 4 <= c["EWG_WS_WAIT_TIMEOUTS_OFFSET"] < 1024
+    header = open(os.path.join(HEADER_DIR, "embedding_wgrad.h")).read()
+    assert re.search(r"#define EWG_NO_ALLOC_SCRATCH_BYTES \(256 << 10\)", header)
+    assert B.NO_ALLOC_SCRATCH_BYTES == 256 << 10
 
 
 def test_position_bits():
@@ -100,9 +103,13 @@ def test_envelope_31_bit_packing():
 
 
 def test_workspace_bytes():
-    assert ewg.workspace_bytes(8192, 7168) > 2 * 8192 // 11 * 7168 * 4
+    # header (1 KiB), a 32-byte record per possible long chunk (2n/11 of them), a
+    # 16-byte record per possible long run (n/11): no per-column storage
+    assert ewg.workspace_bytes(8192, 7168) >= 1024 + 32 * (2 * 8192 // 11) + 16 * (8192 // 11)
+    assert ewg.workspace_bytes(8192, 7168) < 64 * 1024
     assert ewg.workspace_bytes(0, 7) == 0 and ewg.workspace_bytes(8193, 7) == 0
-    assert ewg.workspace_bytes(4096, 1) < ewg.workspace_bytes(4096, 1000)
+    assert ewg.workspace_bytes(4096, 1) == ewg.workspace_bytes(4096, 1000)
+    assert ewg.workspace_bytes(4096, 1) < ewg.workspace_bytes(8192, 1)
 
 
 def test_status_strings():
@@ -302,18 +309,19 @@ def test_library_reads_no_environment_variable():
 
 
 def test_no_alloc_entry_point_checks_sizes_before_any_device_call():
-    """accumulate_embedding_wgrad_no_alloc rejects sizes beyond its static scratch
-    (EWG_SCRATCH_TOO_SMALL) and sizes outside the envelope before it touches a device,
-    so these run without a GPU (the pointers are never dereferenced)."""
+    """accumulate_embedding_wgrad_no_alloc checks its arguments before it touches a
+    device, so these run without a GPU (the pointers are never dereferenced). Every
+    size of the envelope fits its static scratch (the workspace does not grow with
+    hidden), so the scratch-size check is a guard that no valid call reaches."""
     f = B.lib.accumulate_embedding_wgrad_no_alloc
     n = 8192
-    ok = max(h for h in (11008, 7168) if B.workspace_bytes(n, h) <= B.NO_ALLOC_SCRATCH_BYTES)
-    assert ok == 11008
-    too_big = f(8, 8, 8, n, ok + 1, 129280, ok + 1, ok + 1, B.EWG_INT32, B.EWG_BF16,
-                B.EWG_FP32, None)
-    assert too_big == B.EWG_SCRATCH_TOO_SMALL
+    for hidden in (1, 7168, 11009, 1 << 24):
+        assert 0 < B.workspace_bytes(n, hidden) <= B.NO_ALLOC_SCRATCH_BYTES
+    assert B.workspace_bytes(n, 1) == B.workspace_bytes(n, 1 << 24)
     assert f(8, 8, 8, 3072, 128, 512, 128, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
              None) == B.EWG_UNSUPPORTED
     assert f(None, 8, 8, n, 128, 512, 128, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
+             None) == B.EWG_INVALID_ARGUMENT
+    assert f(8, 8, 8, n, 128, 512, 127, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
              None) == B.EWG_INVALID_ARGUMENT
     assert "static scratch" in B.lib.ewg_status_string(B.EWG_SCRATCH_TOO_SMALL).decode()

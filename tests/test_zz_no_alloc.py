@@ -48,21 +48,21 @@ def test_no_alloc_matches_workspace_call_twice(first, second):
         no_alloc_equals_workspace_call(name)
 
 
-def test_no_alloc_rejects_sizes_beyond_the_scratch():
-    """Sizes whose workspace exceeds the static scratch return EWG_SCRATCH_TOO_SMALL
-    before anything is enqueued: main_grad keeps its bits."""
-    n, hidden = 8192, 11009
-    assert ewg.workspace_bytes(n, hidden) > B.NO_ALLOC_SCRATCH_BYTES
-    assert ewg.workspace_bytes(n, hidden - 1) <= B.NO_ALLOC_SCRATCH_BYTES
+def test_no_alloc_rejects_bad_arguments_without_touching_main_grad():
+    """Arguments the call rejects (an unsupported token count, a stride below hidden)
+    return their status before anything is enqueued: main_grad keeps its bits."""
+    n, hidden = 8192, 256
     ids = torch.randint(0, 100, (n,), dtype=torch.int32, device="cuda")
     grad = torch.randn(n, hidden, device="cuda").to(torch.bfloat16)
     mg = torch.randn(100, hidden, device="cuda")
     before = mg.clone()
-    st = B.lib.accumulate_embedding_wgrad_no_alloc(
-        ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), n, hidden, 100, hidden, hidden,
-        B.EWG_INT32, B.EWG_BF16, B.EWG_FP32, torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    f = B.lib.accumulate_embedding_wgrad_no_alloc
+    assert f(ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), 3072, hidden, 100, hidden, hidden,
+             B.EWG_INT32, B.EWG_BF16, B.EWG_FP32, stream) == B.EWG_UNSUPPORTED
+    assert f(ids.data_ptr(), grad.data_ptr(), mg.data_ptr(), n, hidden, 100, hidden - 1, hidden,
+             B.EWG_INT32, B.EWG_BF16, B.EWG_FP32, stream) == B.EWG_INVALID_ARGUMENT
     torch.cuda.synchronize()
-    assert st == B.EWG_SCRATCH_TOO_SMALL
     assert torch.equal(_bits(mg), _bits(before))
-    with pytest.raises(B.EmbeddingWgradError):
-        ewg.accumulate_embedding_wgrad_no_alloc(ids, grad, mg)
+    with pytest.raises(ValueError):
+        ewg.accumulate_embedding_wgrad_no_alloc(ids, grad.t(), mg)
