@@ -65,10 +65,9 @@ constexpr int kBlockStageFloats = 26624; // chunk sums of one column block (104 
 constexpr int kMinBlockLog = 4;          // narrowest column block: 16 columns (64 bytes of fp32)
 constexpr int kMaxBlockLog = 11;         // widest column block: 2048 columns
 constexpr int kFoldCols = (1 << kMaxBlockLog) / kSortThreads;   // fold columns per thread
-constexpr int kLongItems = 1;           // items of a column block a wave has in flight at once
-// grad bytes of a column block: kLongItems items of 10 rows x 64 lanes x 16 bytes
-// for each of the 16 waves, so that a block is about one round of loads
-constexpr uint64_t kBlockBytes = (uint64_t)kLongItems * 16 * kNRows * 64 * 16;
+// grad bytes of a column block: one item of 10 rows x 64 lanes x 16 bytes for
+// each of the 16 waves, so that a block is one round of loads
+constexpr uint64_t kBlockBytes = (uint64_t)kSortWaves * kNRows * 64 * 16;
 static_assert((kMaxRunChunks << kMinBlockLog) <= kBlockStageFloats,
               "the narrowest block of the longest run fits the stage");
 
@@ -91,8 +90,9 @@ struct FollowerSmem {
 struct BlockSmem {
     float stage[kBlockStageFloats];          // chunk sums of one block, [chunk][column]
     u32x4 runs[kMaxLongRuns + 1];            // run records
-    uint16_t pos[kMaxLongChunks * kNRows];   // positions of every long chunk, kNRows each
+    alignas(4) uint16_t pos[kMaxLongChunks * kNRows];   // positions of every long chunk, kNRows each
     uint8_t rows[kMaxLongChunks];            // rows of every long chunk
+    alignas(16) float trash[8];              // the stores of lanes without a piece
 };
 
 union AccSmem {
@@ -332,16 +332,15 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 // log2 of the column-block width of a long run of `chunks` chunks: the widest
 // power of two up to 2048 columns (no wider than hidden needs) whose chunk
 // sums fit the LDS stage and whose grad bytes (at most 10 rows per chunk) stay
-// within `target`, but no narrower than 64 bytes of a grad row (32 bf16 or 16
-// fp32 columns).
-__device__ __forceinline__ int block_log_width(uint32_t chunks, int hidden, uint64_t target,
-                                               int grad_bytes) {
+// within one round of loads of the workgroup, but no narrower than 64 bytes of
+// a grad row (32 bf16 or 16 fp32 columns).
+__device__ __forceinline__ int block_log_width(uint32_t chunks, int hidden, int grad_bytes) {
     const int min_lw = grad_bytes >= 4 ? kMinBlockLog : kMinBlockLog + 1;
     int lw = min_lw;
     while (lw < kMaxBlockLog && (1 << lw) < hidden) ++lw;
     const uint64_t row_bytes = (uint64_t)chunks * kNRows * (uint64_t)grad_bytes;
     while (lw > min_lw &&
-           (((uint64_t)chunks << lw) > (uint64_t)kBlockStageFloats || (row_bytes << lw) > target))
+           (((uint64_t)chunks << lw) > (uint64_t)kBlockStageFloats || (row_bytes << lw) > kBlockBytes))
         --lw;
     return lw;
 }
@@ -456,7 +455,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
         uint32_t blocks = 0, code = 0;
         if (tid < (int)n_lr) {
             const uint32_t chunks = lr[4 * tid + 2];
-            const int lw = block_log_width(chunks, hidden, kBlockBytes, grad_bytes);
+            const int lw = block_log_width(chunks, hidden, grad_bytes);
             blocks = (uint32_t)(((int64_t)hidden + (1 << lw) - 1) >> lw);
             code = chunks | (uint32_t)lw << 16;
         }
@@ -509,116 +508,224 @@ __device__ __forceinline__ bool wave_wait_ready(WsHeader *__restrict__ hdr, uint
     }
 }
 
-// One column block [col0, col0 + min(2^lw, hidden - col0)) of the long run
-// whose `chunks` chunks start at long chunk `first` (main_grad row `row`), by
-// all 1024 threads. Lanes take
-// (chunk, piece) pairs: a row of the block is 2^lw / VEC pieces of VEC
-// columns, a wave covers 64 of them, so several chunks when the block is
-// narrower than 64 pieces and one tile of 64 pieces of one chunk otherwise.
-// Each lane sums its chunk's rows in position order from +0 in fp32 and puts
-// the sums in LDS; after a barrier each column adds its chunk sums in chunk
-// order from +0, rounds once to grad's dtype and is added to main_grad (whose
-// old values were loaded with the first grad loads).
+// One column block [col0, col0 + wc) of the long run whose `chunks` chunks
+// start at long chunk `first` (main_grad row `row`), wc = min(2^lw, hidden -
+// col0). Every thread of the workgroup holds the same description.
+struct BlockDesc {
+    uint32_t row, first, chunks;
+    int lw, col0, wc;
+    bool valid;
+};
+
+// The block of ticket number b: the last run whose first block is at or
+// before b, and the column range b - (that first block) of it. `bad` is set
+// when the record does not describe a block of this call.
+__device__ __forceinline__ BlockDesc describe_block(const BlockSmem &bs, uint32_t b, uint32_t n_lr,
+                                                    uint32_t n_lc, int num_embeddings, int hidden,
+                                                    bool staged_ok, bool *bad) {
+    int lo = 0, hi = (int)n_lr;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (bs.runs[mid].w <= b) lo = mid; else hi = mid;
+    }
+    const u32x4 rec = bs.runs[lo];
+    BlockDesc d;
+    d.row = rec.x;
+    d.first = rec.y;
+    d.chunks = rec.z & 0xffffu;
+    d.lw = (int)((rec.z >> 16) & 0xffu);
+    const bool shape_ok = rec.w <= b && d.lw >= kMinBlockLog && d.lw <= kMaxBlockLog &&
+                          d.chunks > 1u && d.chunks <= (uint32_t)kMaxRunChunks &&
+                          (d.chunks << d.lw) <= (uint32_t)kBlockStageFloats;
+    const int64_t col0 = shape_ok ? (int64_t)(b - rec.w) << d.lw : (int64_t)hidden;
+    d.valid = staged_ok && shape_ok && d.row < (uint32_t)num_embeddings && d.first < n_lc &&
+              d.chunks <= n_lc - d.first && col0 < hidden;
+    *bad = !d.valid;
+    d.col0 = d.valid ? (int)col0 : 0;
+    const int width = 1 << d.lw;
+    d.wc = d.valid ? (hidden - d.col0 < width ? hidden - d.col0 : width) : 0;
+    return d;
+}
+
+// The lanes of a block take (chunk, piece) pairs: a row of the block is
+// 2^lw / VEC pieces of VEC columns and a wave covers 64 of them, so several
+// chunks when the block is narrower than 64 pieces and one tile of 64 pieces
+// of one chunk otherwise. Item `it` of the block is one such wave's worth.
+template <int VEC>
+struct ItemShape {
+    int llog, tlog, per, items;
+    __device__ __forceinline__ ItemShape(int lw, uint32_t chunks) {
+        constexpr int kVecLog = VEC == 8 ? 3 : (VEC == 4 ? 2 : (VEC == 2 ? 1 : 0));
+        static_assert((1 << kVecLog) == VEC, "VEC is 1, 2, 4 or 8");
+        const int plog = lw - kVecLog;   // pieces per row, log2 (>= 2)
+        llog = plog < 6 ? plog : 6;      // lanes per row, log2
+        tlog = plog - llog;              // tiles of 64 pieces per row, log2
+        per = 64 >> llog;                // chunks per wave item
+        items = (((int)chunks + per - 1) / per) << tlog;
+    }
+};
+
+// This lane's part of item `it`: its chunk k, its column lc in the block, and
+// whether the piece is inside the block (active) and whole (VEC columns).
+struct LanePiece {
+    int k, lc, rows;
+    bool active, whole;
+};
+
+template <int VEC>
+__device__ __forceinline__ LanePiece lane_piece(const BlockSmem &bs, const BlockDesc &d,
+                                                const ItemShape<VEC> &sh, int it, int lane) {
+    LanePiece q;
+    q.k = (it >> sh.tlog) * sh.per + (lane >> sh.llog);
+    q.lc = (((it & ((1 << sh.tlog) - 1)) << 6) + (lane & ((1 << sh.llog) - 1))) * VEC;
+    q.active = d.valid && it < sh.items && q.k < (int)d.chunks && q.lc < d.wc;
+    q.whole = q.active && q.lc + VEC <= d.wc;
+    const int rows = (int)bs.rows[q.active ? d.first + q.k : 0u];   // read by every lane
+    q.rows = q.active ? rows : 0;
+    return q;
+}
+
+// The rows of this lane's piece (whole pieces only; see stage_piece). Every
+// load is issued whatever the lane's piece: a row past the chunk's last
+// re-reads its first row and a lane without a whole piece reads grad's first
+// VEC elements, so that the compiler's count of loads in flight is exact and
+// no load waits for an earlier one (a load under a lane condition leaves its
+// register possibly pending, and the next write of that register then waits
+// for every load in flight).
+template <typename GT, int VEC>
+__device__ __forceinline__ void load_piece_rows(const BlockSmem &bs, const BlockDesc &d,
+                                                const LanePiece &q, const GT *__restrict__ grad,
+                                                int64_t grad_stride, GT (&raw)[kNRows][VEC]) {
+    static_assert(kNRows % 2 == 0 && (kNRows * sizeof(uint16_t)) % 4 == 0,
+                  "a chunk's positions are whole 32-bit words");
+    // the chunk's positions as 32-bit words, all LDS reads issued before the first use
+    const uint32_t *pw =
+        reinterpret_cast<const uint32_t *>(&bs.pos[(q.whole ? d.first + q.k : 0u) * kNRows]);
+    uint32_t w[kNRows / 2];
+#pragma unroll
+    for (int i = 0; i < kNRows / 2; ++i) w[i] = pw[i];
+    const GT *base = q.whole ? grad + d.col0 + q.lc : grad;
+#pragma unroll
+    for (int r = 0; r < kNRows; ++r) {
+        const uint32_t pr = r < q.rows ? (w[r >> 1] >> (16 * (r & 1))) & 0xffffu : w[0] & 0xffffu;
+        const int64_t p = q.whole ? (int64_t)pr : 0;
+        load_vec<GT, VEC>(base + p * grad_stride, raw[r]);
+    }
+}
+
+// The chunk sum of a piece from its loaded rows: fp32, from +0, rows in
+// position order, into the LDS stage at [chunk][column]. Every register of
+// `raw` is read and every lane stores (a lane without a whole piece into
+// bs.trash), so that no load result stays pending past this point.
+template <typename G, int VEC>
+__device__ __forceinline__ void stage_piece(BlockSmem &bs, int lw, const LanePiece &q,
+                                            const typename G::T (&raw)[kNRows][VEC]) {
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kNRows; ++r) {
+        const bool take = r < q.rows;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float t = acc[e] + G::widen(raw[r][e]);
+            acc[e] = take ? t : acc[e];
+        }
+    }
+    float *dst = q.whole ? &bs.stage[(q.k << lw) + q.lc] : bs.trash;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
+}
+
+// The ragged end of a row (fewer than VEC columns left), element by element.
+template <typename G, int VEC>
+__device__ __forceinline__ void stage_ragged(BlockSmem &bs, const BlockDesc &d, const LanePiece &q,
+                                             const typename G::T *__restrict__ grad,
+                                             int64_t grad_stride) {
+    const uint16_t *pp = &bs.pos[(d.first + q.k) * kNRows];
+    const typename G::T *gcol = grad + d.col0 + q.lc;
+    for (int e = 0; e < VEC && q.lc + e < d.wc; ++e) {
+        float a = 0.0f;
+        for (int r = 0; r < q.rows; ++r) a = a + G::widen(gcol[(int64_t)pp[r] * grad_stride + e]);
+        bs.stage[(q.k << d.lw) + q.lc + e] = a;
+    }
+}
+
+// Loads of a block issued ahead of its use: the main_grad values its fold
+// adds to (first), then the rows of this wave's first item. Both wait in
+// registers while the workgroup folds the previous block.
 template <typename G, typename M, int VEC>
-__device__ __forceinline__ void long_block(BlockSmem &bs, int lw, uint32_t row, uint32_t first,
-                                           uint32_t chunks, int col0,
-                                           const typename G::T *__restrict__ grad,
-                                           int64_t grad_stride, typename M::T *__restrict__ main_grad,
-                                           int64_t mg_stride, int hidden) {
-    using GT = typename G::T;
-    using MT = typename M::T;
+__device__ __forceinline__ void block_prefetch(const BlockSmem &bs, const BlockDesc &d,
+                                               const typename G::T *__restrict__ grad,
+                                               int64_t grad_stride,
+                                               const typename M::T *__restrict__ main_grad,
+                                               int64_t mg_stride, LanePiece &q,
+                                               typename G::T (&raw)[kNRows][VEC],
+                                               typename M::T (&old)[kFoldCols]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int width = 1 << lw;
-    const int wc = hidden - col0 < width ? hidden - col0 : width;
-    MT *mrow = main_grad + (int64_t)row * mg_stride + col0;
-    MT old[kFoldCols];
+    const typename M::T *mrow = main_grad + (int64_t)d.row * mg_stride + d.col0;
 #pragma unroll
     for (int i = 0; i < kFoldCols; ++i) {
         const int j = tid + i * kSortThreads;
-        if (j < wc) old[i] = mrow[j];
+        if (j < d.wc) old[i] = mrow[j];
     }
-    constexpr int kVecLog = VEC == 8 ? 3 : (VEC == 4 ? 2 : (VEC == 2 ? 1 : 0));
-    static_assert((1 << kVecLog) == VEC, "VEC is 1, 2, 4 or 8");
-    const int plog = lw - kVecLog;                 // pieces per row, log2 (>= 2)
-    const int llog = plog < 6 ? plog : 6;          // lanes per row, log2
-    const int tlog = plog - llog;                  // tiles of 64 pieces per row, log2
-    const int per = 64 >> llog;                    // chunks per wave item
-    const int items = (((int)chunks + per - 1) / per) << tlog;
-    const int kl = lane >> llog;
-    const int pl = lane & ((1 << llog) - 1);
-    // kLongItems items per wave at a time: all their row loads are in flight
-    // before the first add
-    for (int it0 = wave; it0 < items; it0 += kLongItems * kSortWaves) {
-        int k[kLongItems], lc[kLongItems], rows[kLongItems];
-        bool whole[kLongItems], active[kLongItems];
-        const uint16_t *pp[kLongItems];
-        const GT *gcol[kLongItems];
-#pragma unroll
-        for (int q = 0; q < kLongItems; ++q) {
-            const int it = it0 + q * kSortWaves;
-            k[q] = (it >> tlog) * per + kl;
-            lc[q] = (((it & ((1 << tlog) - 1)) << 6) + pl) * VEC;   // column in the block
-            active[q] = it < items && k[q] < (int)chunks && lc[q] < wc;
-            whole[q] = active[q] && lc[q] + VEC <= wc;
-            rows[q] = active[q] ? (int)bs.rows[first + k[q]] : 0;
-            pp[q] = &bs.pos[(first + (active[q] ? k[q] : 0)) * kNRows];
-            gcol[q] = grad + col0 + lc[q];
-        }
-        GT raw[kLongItems][kNRows][VEC];
-#pragma unroll
-        for (int q = 0; q < kLongItems; ++q)
-#pragma unroll
-            for (int r = 0; r < kNRows; ++r)
-                if (whole[q] && r < rows[q])
-                    load_vec<GT, VEC>(gcol[q] + (int64_t)pp[q][r] * grad_stride, raw[q][r]);
-#pragma unroll
-        for (int q = 0; q < kLongItems; ++q) {
-            if (whole[q]) {   // a whole piece
-                float acc[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-#pragma unroll
-                for (int r = 0; r < kNRows; ++r)
-                    if (r < rows[q]) {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + G::widen(raw[q][r][e]);
-                    }
-                float *dst = &bs.stage[(k[q] << lw) + lc[q]];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
-            } else if (active[q]) {   // the ragged end of the row, element by element
-                for (int e = 0; e < VEC && lc[q] + e < wc; ++e) {
-                    float a = 0.0f;
-                    for (int r = 0; r < rows[q]; ++r)
-                        a = a + G::widen(gcol[q][(int64_t)pp[q][r] * grad_stride + e]);
-                    bs.stage[(k[q] << lw) + lc[q] + e] = a;
-                }
-            }
-        }
+    const ItemShape<VEC> sh(d.lw, d.chunks);
+    q = lane_piece<VEC>(bs, d, sh, wave, lane);
+    load_piece_rows<typename G::T, VEC>(bs, d, q, grad, grad_stride, raw);
+}
+
+// The chunk sums of a block into the LDS stage: this wave's first item from
+// the prefetched rows, then its further items (a block of more items than the
+// workgroup has waves) with their loads issued here.
+template <typename G, int VEC>
+__device__ __forceinline__ void block_stage(BlockSmem &bs, const BlockDesc &d, const LanePiece &q,
+                                            const typename G::T (&raw)[kNRows][VEC],
+                                            const typename G::T *__restrict__ grad,
+                                            int64_t grad_stride) {
+    using GT = typename G::T;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    stage_piece<G, VEC>(bs, d.lw, q, raw);
+    if (q.active && !q.whole) stage_ragged<G, VEC>(bs, d, q, grad, grad_stride);
+    const ItemShape<VEC> sh(d.lw, d.chunks);
+    for (int it = wave + kSortWaves; it < sh.items; it += kSortWaves) {   // uniform over the wave
+        const LanePiece e = lane_piece<VEC>(bs, d, sh, it, lane);
+        GT more[kNRows][VEC];
+        load_piece_rows<GT, VEC>(bs, d, e, grad, grad_stride, more);
+        stage_piece<G, VEC>(bs, d.lw, e, more);
+        if (e.active && !e.whole) stage_ragged<G, VEC>(bs, d, e, grad, grad_stride);
     }
-    __syncthreads();
+}
+
+// After the stage is complete: each column adds its chunk sums in chunk order
+// from +0, rounds once to grad's dtype and is added to main_grad (old values
+// from block_prefetch).
+template <typename G, typename M>
+__device__ __forceinline__ void block_fold(const BlockSmem &bs, const BlockDesc &d,
+                                           typename M::T *__restrict__ main_grad, int64_t mg_stride,
+                                           const typename M::T (&old)[kFoldCols]) {
+    const int tid = threadIdx.x;
+    typename M::T *mrow = main_grad + (int64_t)d.row * mg_stride + d.col0;
 #pragma unroll
     for (int i = 0; i < kFoldCols; ++i) {
         const int wave_j0 = (tid & ~63) + i * kSortThreads;
-        if (wave_j0 < wc) {   // uniform over the wave
+        if (wave_j0 < d.wc) {   // uniform over the wave
             const int j = tid + i * kSortThreads;
-            const float *col = &bs.stage[j < wc ? j : wave_j0];
+            const float *col = &bs.stage[j < d.wc ? j : wave_j0];
             float acc = 0.0f;
             // the adds stay in chunk order; the LDS reads of a group of 8 are
             // all issued before the first add
             int k = 0;
-            for (; k + 8 <= (int)chunks; k += 8) {
+            for (; k + 8 <= (int)d.chunks; k += 8) {
                 float v[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = col[(k + q) << lw];
+                for (int u = 0; u < 8; ++u) v[u] = col[(k + u) << d.lw];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) acc = acc + v[q];
+                for (int u = 0; u < 8; ++u) acc = acc + v[u];
             }
-            for (; k < (int)chunks; ++k) acc = acc + col[k << lw];
-            if (j < wc) mrow[j] = finish<G, M>(acc, old[i]);
+            for (; k < (int)d.chunks; ++k) acc = acc + col[k << d.lw];
+            if (j < d.wc) mrow[j] = finish<G, M>(acc, old[i]);
         }
     }
-    __syncthreads();
 }
 
 // Wait for the flag (wave 0); stage the run records and the positions and
@@ -638,6 +745,8 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
                                             typename M::T *__restrict__ main_grad,
                                             int64_t mg_stride, int hidden, uint32_t epoch,
                                             bool take) {
+    using GT = typename G::T;
+    using MT = typename M::T;
     const int tid = threadIdx.x;
     if (tid < 64) {   // wave 0
         uint32_t nb = 0u, lc = 0u, lr = 0u;
@@ -676,36 +785,49 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
     if (tid == 0) s_word[0] = fetch_add_coherent(&hdr->block_ticket, 1u);
     __syncthreads();
     const bool staged_ok = s_word[3] == 0u;   // s_word[3] is not written again
-    for (;;) {
-        const uint32_t b = s_word[0];
-        __syncthreads();   // every thread has read the claim before the next one lands
-        if (b >= n_blocks) break;   // uniform
-        // the next claim travels while this block is processed
-        uint32_t next = 0u;
-        if (tid == 0) next = fetch_add_coherent(&hdr->block_ticket, 1u);
-        // the run of block b: the last run whose first block is at or before b
-        int lo = 0, hi = (int)n_lr;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (bs.runs[mid].w <= b) lo = mid; else hi = mid;
-        }
-        const u32x4 rec = bs.runs[lo];
-        const uint32_t row = rec.x, first = rec.y, chunks = rec.z & 0xffffu;
-        const int lw = (int)((rec.z >> 16) & 0xffu);
-        const bool shape_ok = rec.w <= b && lw >= kMinBlockLog && lw <= kMaxBlockLog &&
-                              chunks > 1u && chunks <= (uint32_t)kMaxRunChunks &&
-                              (chunks << lw) <= (uint32_t)kBlockStageFloats;
-        const int64_t col0 = shape_ok ? (int64_t)(b - rec.w) << lw : (int64_t)hidden;
-        const bool valid = staged_ok && shape_ok && row < (uint32_t)num_embeddings &&
-                           first < n_lc && chunks <= n_lc - first && col0 < hidden;
-        if (valid)   // uniform
-            long_block<G, M, VEC>(bs, lw, row, first, chunks, (int)col0, grad, grad_stride,
-                                  main_grad, mg_stride, hidden);
-        else if (tid == 0)
-            fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), 1u);
-        if (tid == 0) s_word[0] = next;
+    uint32_t b = s_word[0];
+    __syncthreads();   // every thread has read the claim before the next one lands
+    if (b >= n_blocks) return;   // uniform
+    // Software pipeline over the blocks this workgroup takes: the loads of
+    // the next block are in flight while the current one is folded. Per
+    // block: stage its chunk sums; barrier; issue the next block's loads
+    // (its number was claimed one block earlier) and claim the one after;
+    // fold this one; barrier. The main_grad loads of a block are issued
+    // before its grad rows, so the wait for the rows (at its stage) also
+    // covers them and the fold waits on no load in flight.
+    const uint32_t one = (tid == 0) ? 1u : 0u;
+    bool bad_desc = false;
+    BlockDesc d = describe_block(bs, b, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc);
+    uint32_t bad_blocks = bad_desc ? one : 0u;
+    LanePiece q;
+    GT raw[kNRows][VEC];
+    MT old[kFoldCols];
+    block_prefetch<G, M, VEC>(bs, d, grad, grad_stride, main_grad, mg_stride, q, raw, old);
+    uint32_t next = 0u;
+    if (tid == 0) next = fetch_add_coherent(&hdr->block_ticket, 1u);
+    for (int par = 1;; par ^= 1) {
+        block_stage<G, VEC>(bs, d, q, raw, grad, grad_stride);
+        if (tid == 0) s_word[par] = next;   // claimed one block earlier
         __syncthreads();
+        const uint32_t b1 = s_word[par];
+        const bool more = b1 < n_blocks;   // uniform
+        BlockDesc d1 = d;
+        MT old1[kFoldCols];
+        if (more) {
+            d1 = describe_block(bs, b1, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc);
+            if (bad_desc) bad_blocks += one;
+            block_prefetch<G, M, VEC>(bs, d1, grad, grad_stride, main_grad, mg_stride, q, raw, old1);
+            if (tid == 0) next = fetch_add_coherent(&hdr->block_ticket, 1u);
+        }
+        if (d.valid) block_fold<G, M>(bs, d, main_grad, mg_stride, old);
+        __syncthreads();   // the stage is free for the next block; s_word[par] was read
+        if (!more) break;
+        d = d1;
+#pragma unroll
+        for (int i = 0; i < kFoldCols; ++i) old[i] = old1[i];
     }
+    if (bad_blocks)
+        fetch_add_coherent(reinterpret_cast<uint32_t *>(&hdr->wait_timeouts), bad_blocks);
 }
 
 template <typename IdT, typename G, typename M, int VEC>
