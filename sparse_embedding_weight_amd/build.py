@@ -21,6 +21,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE fp32: keep denormals, no contraction, no reassociation
     "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off", "-fno-fast-math",
+    # atomics stay as written: the optimizer's rewrite of a uniform-address
+    # atomic reads its result back at once, which makes a wave wait for every
+    # load it has in flight, and its per-wave reductions cost more than the
+    # LDS atomics they replace here
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -205,29 +205,38 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         }
         // positions in blocked order: thread t owns [8t, 8t + 8), whose slots
         // it reads with one 16-byte load
+        // (the slot, key and count words of the thread's positions are all
+        // read before the first is used)
         const int p0 = tid * kSortItems;
         static_assert(kSortItems == 8, "eight 16-bit slots per thread");
         const u32x4 sw = reinterpret_cast<const u32x4 *>(fs.slot_of_pos)[tid];
         const uint32_t sw4[4] = {sw.x, sw.y, sw.z, sw.w};
+        uint32_t hs[kSortItems], kw[kSortItems], cw[kSortItems];
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            hs[j] = p0 + j < n ? (sw4[j >> 1] >> (16 * (j & 1))) & 0xffffu : kNoSlot;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t a = hs[j] & (uint32_t)(kHashSlots - 1);   // in the table for kNoSlot too
+            kw[j] = fs.key[a];
+            cw[j] = fs.cnt[a];
+        }
         uint32_t v[kSortItems];
         uint32_t sum = 0;
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
-            const int p = p0 + j;
-            v[j] = 0;
-            const uint32_t h = p < n ? (sw4[j >> 1] >> (16 * (j & 1))) & 0xffffu : kNoSlot;
-            if (h != kNoSlot) {
-                const uint32_t c = fs.cnt[h] & 0xffffu;
-                if ((fs.key[h] >> id_shift) == (uint32_t)p && c <= (uint32_t)kNRows)
-                    v[j] = (c * row_cost + end_cost) | (1u << kCostBits);
-            }
+            const uint32_t c = cw[j] & 0xffffu;
+            const bool first_pos = hs[j] != kNoSlot && (kw[j] >> id_shift) == (uint32_t)(p0 + j);
+            v[j] = first_pos && c <= (uint32_t)kNRows ? (c * row_cost + end_cost) | (1u << kCostBits) : 0u;
             sum += v[j];
         }
         uint32_t total;
         const uint32_t run = block_exclusive_scan32(sum, fs.scan32, &total);
-        const uint64_t cost_all = total & kCostMask;
-        const uint64_t lo = cost_all * (uint64_t)me / (uint64_t)followers;
-        const uint64_t hi = cost_all * (uint64_t)(me + 1) / (uint64_t)followers;
+        // cost_all < 2^kCostBits and followers < 2^12: 32-bit products
+        const uint32_t cost_all = total & kCostMask;
+        const uint32_t lo = cost_all * (uint32_t)me / (uint32_t)followers;
+        const uint32_t hi = cost_all * (uint32_t)(me + 1) / (uint32_t)followers;
+        static_assert((uint64_t)kCostMask * (kMaxGrid + 1) < (1ull << 32), "32-bit share bounds");
         // runs are numbered in position order; this follower's (cost start in
         // [lo, hi)) are a contiguous range of numbers
         {
@@ -235,7 +244,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             uint32_t mine = 0;
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j) {
-                const uint64_t start = x & kCostMask;
+                const uint32_t start = x & kCostMask;
                 if (v[j] && start >= lo && start < hi) {
                     atomicMin(&fs.first_rank, x >> kCostBits);
                     ++mine;
@@ -251,15 +260,14 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
             uint32_t x = run;
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j) {
-                const uint64_t start = x & kCostMask;
+                const uint32_t start = x & kCostMask;
                 if (v[j] && start >= lo && start < hi) {
                     const int li = (int)((x >> kCostBits) - first) - r0;
                     if (li >= 0 && li < kOwnedMax) {
-                        const uint32_t h = fs.slot_of_pos[p0 + j];
-                        fs.run_id[li] = (fs.key[h] & id_mask) - 1u;
+                        fs.run_id[li] = (kw[j] & id_mask) - 1u;
                         fs.run_len[li] = 0u;
-                        fs.run_slot[li] = h;
-                        fs.cnt[h] |= (uint32_t)(li + 1) << 16;
+                        fs.run_slot[li] = hs[j];
+                        fs.cnt[hs[j]] |= (uint32_t)(li + 1) << 16;
                     }
                 }
                 x += v[j];
@@ -271,15 +279,17 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
         const bool last_round = total_mine - r0 <= kOwnedMax;
 
         // gather the positions of the round's runs, then put each run in order
+        {
+            uint32_t m[kSortItems], k[kSortItems];
 #pragma unroll
-        for (int i = 0; i < kSortItems; ++i) {
-            const int p = i * kSortThreads + tid;
-            if (p >= n || fs.slot_of_pos[p] == kNoSlot) continue;
-            const uint32_t m = fs.cnt[fs.slot_of_pos[p]] >> 16;
-            if (m) {
-                const uint32_t k = atomicAdd(&fs.run_len[m - 1u], 1u);
-                fs.run_pos[m - 1u][k] = (uint16_t)p;
-            }
+            for (int j = 0; j < kSortItems; ++j)
+                m[j] = hs[j] != kNoSlot ? fs.cnt[hs[j]] >> 16 : 0u;   // run of the round + 1, or 0
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j)
+                if (m[j]) k[j] = atomicAdd(&fs.run_len[m[j] - 1u], 1u);
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j)
+                if (m[j]) fs.run_pos[m[j] - 1u][k[j]] = (uint16_t)(p0 + j);
         }
         __syncthreads();
         if (tid < n_round) {
