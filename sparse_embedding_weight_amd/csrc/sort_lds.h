@@ -58,18 +58,45 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-    uint32_t lo = __shfl_up((uint32_t)v, d, 64);
-    uint32_t hi = __shfl_up((uint32_t)(v >> 32), d, 64);
+// Inclusive prefix sums over the 64 lanes of a wave with DPP moves (GFX9):
+// row_shr:1, 2, 4 and 8 sum inside each row of 16 lanes (a lane with no
+// source reads 0), then row_bcast:15 adds the last lane of rows 0 and 2 to
+// rows 1 and 3, and row_bcast:31 adds lane 31 to rows 2 and 3 (a row outside
+// the row mask keeps the 0 it started from). Every lane of the wave must be
+// active.
+constexpr int kDppRowShr = 0x110;       // + shift (1..15)
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_take(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_take64(uint64_t v) {
+    const uint32_t lo = dpp_take<CTRL, ROW_MASK>((uint32_t)v);
+    const uint32_t hi = dpp_take<CTRL, ROW_MASK>((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint64_t o = shfl_up_u64(v, d);
-        if (lane >= d) v += o;
-    }
+__device__ __forceinline__ uint32_t wave_inclusive_scan32(uint32_t v) {
+    v += dpp_take<kDppRowShr + 1, 0xf>(v);
+    v += dpp_take<kDppRowShr + 2, 0xf>(v);
+    v += dpp_take<kDppRowShr + 4, 0xf>(v);
+    v += dpp_take<kDppRowShr + 8, 0xf>(v);
+    v += dpp_take<kDppRowBcast15, 0xa>(v);
+    v += dpp_take<kDppRowBcast31, 0xc>(v);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t v, int /*lane*/) {
+    v += dpp_take64<kDppRowShr + 1, 0xf>(v);
+    v += dpp_take64<kDppRowShr + 2, 0xf>(v);
+    v += dpp_take64<kDppRowShr + 4, 0xf>(v);
+    v += dpp_take64<kDppRowShr + 8, 0xf>(v);
+    v += dpp_take64<kDppRowBcast15, 0xa>(v);
+    v += dpp_take64<kDppRowBcast31, 0xc>(v);
     return v;
 }
 
@@ -98,22 +125,12 @@ __device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t *s
 __device__ __forceinline__ uint32_t block_exclusive_scan32(uint32_t v, uint32_t *s_tmp,
                                                            uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += o;
-    }
+    const uint32_t inc = wave_inclusive_scan32(v);
     if (lane == 63) s_tmp[wave] = inc;
     __syncthreads();
     if (wave == 0) {
         const uint32_t w = lane < kSortWaves ? s_tmp[lane] : 0u;
-        uint32_t wi = w;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(wi, d, 64);
-            if (lane >= d) wi += o;
-        }
+        const uint32_t wi = wave_inclusive_scan32(w);
         if (lane < kSortWaves) s_tmp[lane] = wi - w;
         if (lane == kSortWaves - 1) s_tmp[kSortWaves] = wi;
     }
