@@ -392,6 +392,108 @@ __device__ __forceinline__ bool kept_id_exceeds_rows(SortSmem &ss, int pos_bits)
     return ss.long_seen != 0;
 }
 
+// The runs of the sorted keys that the long phase needs, for the sorting
+// workgroup (the inspection entry point marks every run with mark_runs in
+// sort_lds.h). Blocked arrangement: thread t owns sorted slots [8t, 8t + 8).
+// Out, in LDS: per long chunk c its first slot and rows (lc_info[c] = slot |
+// (rows - 1) << 13) and its long run (lc_run[c]); per long run r {main_grad
+// row, first long chunk, chunk count, 0} (lr[4r .. 4r + 3]). Every LDS read
+// of a step is issued before the first use, and the two scans are wave-level
+// DPP scans. Line 0 of the header gets the counts (invalid_ids = 0).
+struct LongRuns {
+    int n_long, n_long_chunks;
+};
+
+__device__ __forceinline__ LongRuns mark_long_runs(SortSmem &sm, int cur, int n, int pos_bits,
+                                                   uint32_t *lc_info, uint32_t *lc_run,
+                                                   uint32_t *lr, WsHeader *__restrict__ hdr) {
+    const int tid = threadIdx.x;
+    const uint32_t *sk = sm.keys[cur];
+    const int s0 = tid * kSortItems;
+    uint32_t k[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) k[j] = sk[s0 + j];
+    uint32_t prev = s0 > 0 ? (sk[s0 - 1] >> pos_bits) : 0u;
+    uint32_t start_bits = 0, nstart = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t id = k[j] >> pos_bits;
+        const bool st = s0 + j < n && (s0 + j == 0 || id != prev);
+        start_bits |= (uint32_t)st << j;
+        nstart += st;
+        prev = id;
+    }
+    uint32_t num_runs;
+    const uint32_t run_base =
+        block_exclusive_scan32(nstart, reinterpret_cast<uint32_t *>(sm.scan), &num_runs);
+    // first slot of every run, plus n after the last: runs are [rs[r], rs[r+1])
+    uint32_t *rs = sm.aux;
+    uint32_t run_of[kSortItems];
+    {
+        uint32_t r = run_base;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            if ((start_bits >> j) & 1u) rs[r++] = (uint32_t)(s0 + j);
+            run_of[j] = r > 0u ? r - 1u : 0u;   // in [0, num_runs): slot 0 starts a run
+        }
+    }
+    if (tid == 0) rs[num_runs] = (uint32_t)n;
+    __syncthreads();
+    uint32_t f[kSortItems], e[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        f[j] = rs[run_of[j]];
+        e[j] = rs[run_of[j] + 1u];
+    }
+    // per slot: bit 0 = first slot of a long chunk, bit 16 = first slot of a
+    // long run, bit 32 = first slot of a chunk of any run
+    uint64_t flag[kSortItems], nflag = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t sj = (uint32_t)(s0 + j), off = sj - f[j];
+        const bool valid = s0 + j < n;
+        const bool longer = valid && e[j] - f[j] > (uint32_t)kNRows;
+        const bool chunk_start = valid && off % kNRows == 0u;
+        flag[j] = (uint64_t)(chunk_start && longer) | ((uint64_t)(longer && off == 0u) << 16) |
+                  ((uint64_t)chunk_start << 32);
+        nflag += flag[j];
+    }
+    uint64_t totals;
+    uint64_t idx = block_exclusive_scan(nflag, sm.scan, &totals);
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t sj = (uint32_t)(s0 + j);
+        const uint32_t lc = (uint32_t)(idx & 0xffffu), r = (uint32_t)((idx >> 16) & 0xffffu);
+        const bool run_start = (flag[j] >> 16) & 1u;
+        if (flag[j] & 1u) {
+            const uint32_t left = e[j] - sj;
+            lc_info[lc] = sj | ((left < (uint32_t)kNRows ? left : (uint32_t)kNRows) - 1u) << 13;
+            // a long chunk belongs to the long run that starts at its slot,
+            // or else to the last one started before it
+            lc_run[lc] = run_start ? r : r - 1u;
+        }
+        if (run_start) {
+            lr[4 * r + 0] = k[j] >> pos_bits;
+            lr[4 * r + 1] = lc;
+            lr[4 * r + 2] = (e[j] - f[j] + kNRows - 1) / kNRows;
+            lr[4 * r + 3] = 0u;
+        }
+        idx += flag[j];
+    }
+    LongRuns res;
+    res.n_long_chunks = (int)(totals & 0xffffu);
+    res.n_long = (int)((totals >> 16) & 0xffffu);
+    if (tid == 0) {
+        hdr->invalid_ids = 0;
+        hdr->num_chunks = (int32_t)(totals >> 32);
+        hdr->num_long_runs = res.n_long;
+        hdr->num_long_chunks = res.n_long_chunks;
+        hdr->num_runs = (int32_t)num_runs;
+    }
+    __syncthreads();   // the long-run tables are complete
+    return res;
+}
+
 // Sort, mark runs, write the unit and run records (with the width of each
 // run's column blocks), zero the block ticket, publish the counts and raise
 // the flag. With an id out of
@@ -421,7 +523,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
             hdr->num_long_chunks = 0;
         }
     } else {
-        const int cur = radix_sort_ids(ss, pos_bits, id_bits);
+        const int cur = radix_sort_ids(ss, pos_bits, id_bits, n);
         // after the sort, aux holds: the run of every long chunk, the long-run
         // list (4 words each) and the chunk word of every long chunk
         uint32_t *lc_run = ss.aux;
@@ -430,14 +532,7 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
         static_assert(kMaxLongChunks <= 2048 && 2048 + 4 * kMaxLongRuns <= 8192 &&
                           8192 + kMaxLongChunks <= (kSortWaves << kMaxDigitBits),
                       "long-run tables fit the sort's counter space");
-        const SortOutputs out = {{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}, hdr,
-                                 lc_run, lr};
-        const SortResult res = mark_runs(ss, cur, ss.n_keys, pos_bits, out);
-        for (int c = tid; c < res.n_chunks; c += kSortThreads) {
-            const uint32_t x = res.chunk_info[c];
-            if (x & kInfoLong) lc_info[info_long_chunk(x)] = x;
-        }
-        __syncthreads();
+        const LongRuns res = mark_long_runs(ss, cur, ss.n_keys, pos_bits, lc_info, lc_run, lr, hdr);
         n_lc = (uint32_t)res.n_long_chunks;
         n_lr = (uint32_t)res.n_long;
 
@@ -450,8 +545,8 @@ __device__ __forceinline__ void leader_publish(SortSmem &ss, const IdT *__restri
             uint32_t w[8];
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
-                const uint32_t a = 2 * i < rows ? res.keys[f + 2 * i] & pos_mask : 0u;
-                const uint32_t b = 2 * i + 1 < rows ? res.keys[f + 2 * i + 1] & pos_mask : 0u;
+                const uint32_t a = 2 * i < rows ? ss.keys[cur][f + 2 * i] & pos_mask : 0u;
+                const uint32_t b = 2 * i + 1 < rows ? ss.keys[cur][f + 2 * i + 1] & pos_mask : 0u;
                 w[i] = a | (b << 16);
             }
             w[5] = (uint32_t)rows | (lc_run[c] << 16);

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kSortThreads) void tile_sort_kernel(const IdT *__re
     const int t = blockIdx.x, base = t * kTileKeys;
     const int nt = n - base < kTileKeys ? n - base : kTileKeys;
     const int bad = load_keys<IdT>(sm, ids + base, nt, num_embeddings, kTileBits, 0, false);
-    const int cur = radix_sort_ids(sm, kTileBits, id_bits);
+    const int cur = radix_sort_ids(sm, kTileBits, id_bits, nt);
     for (int i = threadIdx.x; i < nt; i += kSortThreads) tkeys[base + i] = sm.keys[cur][i];
     if (threadIdx.x == 0) hdr->tile_bad[t] = bad;
 }

@@ -191,7 +191,7 @@ __device__ __forceinline__ int load_keys(SortSmem &sm, const IdT *__restrict__ i
 
 // Stable LSD radix passes over the id bits. Returns the buffer that holds
 // the sorted keys.
-__device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id_bits) {
+__device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id_bits, int n) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int cur = 0;
     const int npass = (id_bits + kMaxDigitBits - 1) / kMaxDigitBits;
@@ -214,6 +214,14 @@ __device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id
             dig[i] = (key[i] >> shift) & mask;
             peers[i] = ~0ull;
         }
+        // Slots [n, kMaxTokens) hold padding keys (all ones) in every pass: they
+        // come after every position and each pass is stable. A wave of them
+        // only ranks them in order, with the largest digit.
+        if (wave * kWaveSlots >= n) {   // uniform over the wave
+#pragma unroll
+            for (int i = 0; i < kSortItems; ++i) rank[i] = (uint32_t)(i * 64 + lane);
+            if (lane == 0) cnt[mask] = (uint32_t)kWaveSlots;   // after the clearing above
+        } else {
         // lanes of the same 64-key group with the same digit (8 groups in flight)
         for (int b = 0; b < bits; ++b) {
 #pragma unroll
@@ -223,15 +231,24 @@ __device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id
                 peers[i] &= set ? bal : ~bal;
             }
         }
-        __builtin_amdgcn_wave_barrier();
+        // The lowest lane of each digit adds the digit's keys of the group to
+        // the wave's counter and gets back the count of earlier groups (the
+        // LDS executes one wave's instructions in order, so the 8 adds need no
+        // wait between them); its peers take that base from it.
+        uint32_t base[kSortItems];
 #pragma unroll
         for (int i = 0; i < kSortItems; ++i) {
-            const uint32_t below = popc_below(peers[i]);
-            const uint32_t base = cnt[dig[i]];
-            rank[i] = base + below;
-            __builtin_amdgcn_wave_barrier();
-            if (below == 0) cnt[dig[i]] = base + (uint32_t)__popcll(peers[i]);
-            __builtin_amdgcn_wave_barrier();
+            base[i] = 0u;
+            if (popc_below(peers[i]) == 0u)
+                base[i] = atomicAdd(&cnt[dig[i]], (uint32_t)__popcll(peers[i]));
+            __builtin_amdgcn_wave_barrier();   // group order (free: the wave runs in lockstep)
+        }
+#pragma unroll
+        for (int i = 0; i < kSortItems; ++i) {
+            const int leader = (int)__builtin_ctzll(peers[i]);   // peers holds this lane
+            rank[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(leader << 2, (int)base[i]) +
+                      popc_below(peers[i]);
+        }
         }
         __syncthreads();
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_tokens_kernel(
         report_invalid(out, bad);
         return;
     }
-    const int cur = radix_sort_ids(sm, pos_bits, id_bits);
+    const int cur = radix_sort_ids(sm, pos_bits, id_bits, n);
     mark_runs(sm, cur, n, pos_bits, out);
 }
 
