@@ -342,10 +342,14 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
 // log2 of the column-block width of a long run of `chunks` chunks: the widest
 // power of two up to 2048 columns (no wider than hidden needs) whose chunk
 // sums fit the LDS stage and whose grad bytes (at most 10 rows per chunk) stay
-// within one round of loads of the workgroup, but no narrower than 64 bytes of
-// a grad row (32 bf16 or 16 fp32 columns).
+// within one round of loads of the workgroup, but no narrower than 128 bytes
+// of a grad row (64 bf16 or 32 fp32 columns: memory moves whole 128-byte
+// lines), or 64 bytes where the chunk sums of 128 would not fit the stage. A
+// deep run's block may then take several rounds of loads (block_stage).
 __device__ __forceinline__ int block_log_width(uint32_t chunks, int hidden, int grad_bytes) {
-    const int min_lw = grad_bytes >= 4 ? kMinBlockLog : kMinBlockLog + 1;
+    // 128 bytes of a grad row when the chunk sums fit the stage, else 64
+    const int lw128 = grad_bytes >= 4 ? kMinBlockLog + 1 : kMinBlockLog + 2;
+    const int min_lw = ((uint64_t)chunks << lw128) <= (uint64_t)kBlockStageFloats ? lw128 : lw128 - 1;
     int lw = min_lw;
     while (lw < kMaxBlockLog && (1 << lw) < hidden) ++lw;
     const uint64_t row_bytes = (uint64_t)chunks * kNRows * (uint64_t)grad_bytes;
