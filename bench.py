@@ -109,11 +109,37 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+def strip_c_comments(text):
+    """C/C++ source without its comments and with runs of whitespace made one space, so
+    that an edit of comments or layout alone leaves the kernel hash unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """Hash of the fused kernel's sources, comments and layout aside."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_embedding_weight_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_embedding_weight_amd", "csrc", name)) as f:
+            h.update(strip_c_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,11 +10,11 @@
  * touching only the rows of main_grad whose id occurs in ids, with the
  * arithmetic of the sort-based dense backward (introduction, first bullet)
  * followed by main_grad.add_ (second bullet):
- *   - token ids are sorted together with their positions;
- *   - the grad rows of one id are summed in position order into fp32 partial
- *     sums of at most 10 rows (chunks counted from the first row of the id);
- *   - the partial sums are added in order starting from 0 and the total is
- *     rounded once (round to nearest even) to grad's dtype;
+ *   - the rows of one id are taken by ascending position;
+ *   - they are cut into chunks of ten rows (the last chunk may be shorter),
+ *     counted from the id's first row, and each chunk is summed in fp32;
+ *   - the chunk sums are folded left to right from +0 and the total is
+ *     converted once (round to nearest even) to grad's dtype;
  *   - that value is added to the main_grad row in fp32 and the sum rounded to
  *     main_grad's dtype.
  * Rows of ids that do not occur are neither read nor written (the sentence
@@ -51,7 +51,7 @@ extern "C" {
 
 /* Envelope (page, Data: MIN_TOKENS, MAX_TOKENS, _NROWS). MIN_TOKENS is the
  * smallest token count that takes PyTorch's sort-based path (page,
- * introduction: that path starts above 3072 tokens). */
+ * introduction: 3072 tokens or fewer take another path). */
 #define EWG_MIN_TOKENS 3073
 #define EWG_MAX_TOKENS 8192
 #define EWG_NROWS 10

@@ -3,10 +3,11 @@
 // 1024-thread workgroup per compute unit (at least two workgroups).
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
-// introduction's two bullets (sort the ids with their positions, sum each
-// token's rows in position order into fp32 partial sums of up to 10 rows, add
-// the partial sums in order from 0, round once to the gradient dtype, add in
-// fp32 into main_grad and round to its dtype), _sort_tokens_kernel,
+// introduction's two bullets (equal ids ordered by ascending position; fp32
+// chunk sums of ten consecutive rows or fewer; those sums folded left to
+// right from +0 with a single conversion to grad's dtype at the end; then an
+// fp32 add onto the main_grad row, converted back to main_grad's dtype),
+// _sort_tokens_kernel,
 // _partial_sums_kernel (a run of at most NROWS rows is finished there) and
 // _long_run_sums_kernel (the partial sums of a longer run added in order).
 //

@@ -5,9 +5,9 @@
 // fold of a long run's partial rows in chunk order.
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
-// introduction (fp32 partial sums of up to 10 rows in position order, added
-// in order from 0, one rounding to the gradient dtype, the add into main_grad
-// in fp32), _partial_sums_kernel and _long_run_sums_kernel.
+// introduction (fp32 chunk sums of ten consecutive rows or fewer, folded left
+// to right from +0 with one conversion to grad's dtype, then an fp32 update
+// of main_grad), _partial_sums_kernel and _long_run_sums_kernel.
 #pragma once
 
 #include "ewg_device.h"

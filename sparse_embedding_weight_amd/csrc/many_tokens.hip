@@ -5,10 +5,10 @@
 // depends only on the ones before it, so no workgroup waits for another.
 //
 // Megatron-Core API docs, "core.fusions.fused_embedding_wgrad": the
-// introduction (ids sorted with their positions; each id's rows summed in
-// position order into fp32 partial sums of up to 10 rows counted from its
-// first row, the partial sums added in order from 0, one rounding to the
-// gradient dtype, the add into main_grad in fp32), _sort_tokens_kernel,
+// introduction (equal ids ordered by ascending position; fp32 chunk sums of
+// ten consecutive rows or fewer, the chunks counted from an id's first row;
+// those sums folded left to right from +0 and converted once to grad's dtype;
+// the main_grad update done in fp32), _sort_tokens_kernel,
 // _partial_sums_kernel and _long_run_sums_kernel. The one-program sort of at
 // most 8192 keys is what bounds MAX_TOKENS there; nothing in the arithmetic
 // depends on that bound.

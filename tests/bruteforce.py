@@ -7,9 +7,10 @@ construction. Sums are numpy float32 element-wise adds (one IEEE binary32 add
 each); rounding to bf16 is torch's CPU conversion, not the oracle's routine.
 
 Arithmetic followed: Megatron-Core API docs, "core.fusions.fused_embedding_wgrad",
-introduction (chunks of up to 10 rows summed in fp32 in position order, the
-chunk sums added in order from 0, one rounding to the grad dtype, an fp32 add
-into main_grad and a rounding to its dtype) and the _partial_sums_kernel
+introduction (each id's rows by ascending position, cut into fp32-summed
+chunks of ten or fewer; the chunk sums folded left to right from +0 and
+converted once to the grad dtype; an fp32 update of main_grad converted back
+to its dtype) and the _partial_sums_kernel
 docstring (a run of at most 10 rows is one chunk).
 """
 import numpy as np

@@ -325,3 +325,19 @@ def test_no_alloc_entry_point_checks_sizes_before_any_device_call():
     assert f(8, 8, 8, n, 128, 512, 127, 128, B.EWG_INT32, B.EWG_BF16, B.EWG_FP32,
              None) == B.EWG_INVALID_ARGUMENT
     assert "static scratch" in B.lib.ewg_status_string(B.EWG_SCRATCH_TOO_SMALL).decode()
+
+
+def test_kernel_hash_ignores_comments_only():
+    # the counter summaries stay valid across comment edits, never across code edits
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    s = bench.strip_c_comments
+    a = 'int x = 1; // one\n/* block\n comment */ const char* p = "a // b /* c */";\n'
+    b = 'int x = 1;\nconst char* p = "a // b /* c */"; // other words\n'
+    assert s(a) == s(b)
+    assert s(a) != s(a.replace("x = 1", "x = 2"))
+    assert s("c = '\\'';// q\n") == "c = '\\'';"
+    assert len(bench.kernel_source_hash()) == 16
