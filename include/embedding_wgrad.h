@@ -119,6 +119,17 @@ int can_accumulate_embedding_wgrad(int64_t num_tokens, int64_t hidden, int64_t n
  */
 #define EWG_WS_WAIT_TIMEOUTS_OFFSET 144
 
+/*
+ * Byte offset of a third int32 word of the workspace: the device-side bounds
+ * checks that failed since the workspace was zero-filled. It stays 0 in the
+ * default build. A build with -DEWG_DEVICE_CHECKS=1 (a debugging aid) checks
+ * the data-derived indices of the one-kernel path (LDS tables, staged chunk
+ * sums, positions and rows of long-run chunks) against their bounds; an index
+ * out of bounds is counted here and replaced by the last valid one, so that
+ * such a build never accesses memory out of bounds.
+ */
+#define EWG_WS_CHECK_FAILURES_OFFSET 148
+
 size_t accumulate_embedding_wgrad_workspace_bytes(int64_t num_tokens, int64_t hidden);
 
 /*

@@ -407,6 +407,7 @@ def invalid_id_count(workspace: torch.Tensor) -> int:
 
 
 WS_WAIT_TIMEOUTS_OFFSET = 144   # EWG_WS_WAIT_TIMEOUTS_OFFSET
+WS_CHECK_FAILURES_OFFSET = 148  # EWG_WS_CHECK_FAILURES_OFFSET (0 unless built with device checks)
 
 
 def wait_timeouts(workspace: torch.Tensor) -> int:

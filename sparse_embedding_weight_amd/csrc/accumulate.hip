@@ -127,7 +127,7 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
                                                     int64_t grad_stride,
                                                     typename M::T *__restrict__ main_grad,
                                                     int64_t mg_stride, int hidden, int tiles,
-                                                    int me, int followers) {
+                                                    int me, int followers, int32_t *fails) {
     const int tid = threadIdx.x;
     constexpr int kSlotsPerThread = kHashSlots / kSortThreads;
     const int id_shift = 32 - pos_bits;
@@ -287,10 +287,12 @@ __device__ __forceinline__ void follower_short_runs(FollowerSmem &fs, const IdT 
                 m[j] = hs[j] != kNoSlot ? fs.cnt[hs[j]] >> 16 : 0u;   // run of the round + 1, or 0
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j)
-                if (m[j]) k[j] = atomicAdd(&fs.run_len[m[j] - 1u], 1u);
+                if (m[j]) k[j] = atomicAdd(&fs.run_len[checked_index<uint32_t>(m[j] - 1u, kOwnedMax, fails)], 1u);
 #pragma unroll
             for (int j = 0; j < kSortItems; ++j)
-                if (m[j]) fs.run_pos[m[j] - 1u][k[j]] = (uint16_t)(p0 + j);
+                if (m[j])
+                    fs.run_pos[checked_index<uint32_t>(m[j] - 1u, kOwnedMax, fails)]
+                              [checked_index<uint32_t>(k[j], kNRows, fails)] = (uint16_t)(p0 + j);
         }
         __syncthreads();
         if (tid < n_round) {
@@ -625,6 +627,7 @@ struct BlockDesc {
     uint32_t row, first, chunks;
     int lw, col0, wc;
     bool valid;
+    int32_t *fails;   // the header's check_failures word (checked builds)
 };
 
 // The block of ticket number b: the last run whose first block is at or
@@ -632,7 +635,7 @@ struct BlockDesc {
 // when the record does not describe a block of this call.
 __device__ __forceinline__ BlockDesc describe_block(const BlockSmem &bs, uint32_t b, uint32_t n_lr,
                                                     uint32_t n_lc, int num_embeddings, int hidden,
-                                                    bool staged_ok, bool *bad) {
+                                                    bool staged_ok, bool *bad, int32_t *fails) {
     int lo = 0, hi = (int)n_lr;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -640,6 +643,7 @@ __device__ __forceinline__ BlockDesc describe_block(const BlockSmem &bs, uint32_
     }
     const u32x4 rec = bs.runs[lo];
     BlockDesc d;
+    d.fails = fails;
     d.row = rec.x;
     d.first = rec.y;
     d.chunks = rec.z & 0xffffu;
@@ -690,7 +694,8 @@ __device__ __forceinline__ LanePiece lane_piece(const BlockSmem &bs, const Block
     q.lc = (((it & ((1 << sh.tlog) - 1)) << 6) + (lane & ((1 << sh.llog) - 1))) * VEC;
     q.active = d.valid && it < sh.items && q.k < (int)d.chunks && q.lc < d.wc;
     q.whole = q.active && q.lc + VEC <= d.wc;
-    const int rows = (int)bs.rows[q.active ? d.first + q.k : 0u];   // read by every lane
+    const int rows = (int)bs.rows[checked_index<uint32_t>(q.active ? d.first + q.k : 0u,
+                                                          kMaxLongChunks, d.fails)];   // every lane reads
     q.rows = q.active ? rows : 0;
     return q;
 }
@@ -709,8 +714,8 @@ __device__ __forceinline__ void load_piece_rows(const BlockSmem &bs, const Block
     static_assert(kNRows % 2 == 0 && (kNRows * sizeof(uint16_t)) % 4 == 0,
                   "a chunk's positions are whole 32-bit words");
     // the chunk's positions as 32-bit words, all LDS reads issued before the first use
-    const uint32_t *pw =
-        reinterpret_cast<const uint32_t *>(&bs.pos[(q.whole ? d.first + q.k : 0u) * kNRows]);
+    const uint32_t *pw = reinterpret_cast<const uint32_t *>(
+        &bs.pos[checked_index<uint32_t>(q.whole ? d.first + q.k : 0u, kMaxLongChunks, d.fails) * kNRows]);
     uint32_t w[kNRows / 2];
 #pragma unroll
     for (int i = 0; i < kNRows / 2; ++i) w[i] = pw[i];
@@ -729,7 +734,8 @@ __device__ __forceinline__ void load_piece_rows(const BlockSmem &bs, const Block
 // bs.trash), so that no load result stays pending past this point.
 template <typename G, int VEC>
 __device__ __forceinline__ void stage_piece(BlockSmem &bs, int lw, const LanePiece &q,
-                                            const typename G::T (&raw)[kNRows][VEC]) {
+                                            const typename G::T (&raw)[kNRows][VEC],
+                                            int32_t *fails) {
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
@@ -742,7 +748,8 @@ __device__ __forceinline__ void stage_piece(BlockSmem &bs, int lw, const LanePie
             acc[e] = take ? t : acc[e];
         }
     }
-    float *dst = q.whole ? &bs.stage[(q.k << lw) + q.lc] : bs.trash;
+    float *dst = q.whole ? &bs.stage[checked_index((q.k << lw) + q.lc, kBlockStageFloats - VEC + 1, fails)]
+                         : bs.trash;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
 }
@@ -752,12 +759,12 @@ template <typename G, int VEC>
 __device__ __forceinline__ void stage_ragged(BlockSmem &bs, const BlockDesc &d, const LanePiece &q,
                                              const typename G::T *__restrict__ grad,
                                              int64_t grad_stride) {
-    const uint16_t *pp = &bs.pos[(d.first + q.k) * kNRows];
+    const uint16_t *pp = &bs.pos[checked_index<uint32_t>(d.first + q.k, kMaxLongChunks, d.fails) * kNRows];
     const typename G::T *gcol = grad + d.col0 + q.lc;
     for (int e = 0; e < VEC && q.lc + e < d.wc; ++e) {
         float a = 0.0f;
         for (int r = 0; r < q.rows; ++r) a = a + G::widen(gcol[(int64_t)pp[r] * grad_stride + e]);
-        bs.stage[(q.k << d.lw) + q.lc + e] = a;
+        bs.stage[checked_index((q.k << d.lw) + q.lc + e, kBlockStageFloats, d.fails)] = a;
     }
 }
 
@@ -794,14 +801,14 @@ __device__ __forceinline__ void block_stage(BlockSmem &bs, const BlockDesc &d, c
                                             int64_t grad_stride) {
     using GT = typename G::T;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    stage_piece<G, VEC>(bs, d.lw, q, raw);
+    stage_piece<G, VEC>(bs, d.lw, q, raw, d.fails);
     if (q.active && !q.whole) stage_ragged<G, VEC>(bs, d, q, grad, grad_stride);
     const ItemShape<VEC> sh(d.lw, d.chunks);
     for (int it = wave + kSortWaves; it < sh.items; it += kSortWaves) {   // uniform over the wave
         const LanePiece e = lane_piece<VEC>(bs, d, sh, it, lane);
         GT more[kNRows][VEC];
         load_piece_rows<GT, VEC>(bs, d, e, grad, grad_stride, more);
-        stage_piece<G, VEC>(bs, d.lw, e, more);
+        stage_piece<G, VEC>(bs, d.lw, e, more, d.fails);
         if (e.active && !e.whole) stage_ragged<G, VEC>(bs, d, e, grad, grad_stride);
     }
 }
@@ -907,7 +914,9 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
     // covers them and the fold waits on no load in flight.
     const uint32_t one = (tid == 0) ? 1u : 0u;
     bool bad_desc = false;
-    BlockDesc d = describe_block(bs, b, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc);
+    int32_t *fails = &hdr->check_failures;
+    BlockDesc d = describe_block(bs, b, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc,
+                                 fails);
     uint32_t bad_blocks = bad_desc ? one : 0u;
     LanePiece q;
     GT raw[kNRows][VEC];
@@ -924,7 +933,8 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
         BlockDesc d1 = d;
         MT old1[kFoldCols];
         if (more) {
-            d1 = describe_block(bs, b1, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc);
+            d1 = describe_block(bs, b1, n_lr, n_lc, num_embeddings, hidden, staged_ok, &bad_desc,
+                                fails);
             if (bad_desc) bad_blocks += one;
             block_prefetch<G, M, VEC>(bs, d1, grad, grad_stride, main_grad, mg_stride, q, raw, old1);
             if (tid == 0) next = fetch_add_coherent(&hdr->block_ticket, 1u);
@@ -964,7 +974,8 @@ __global__ __launch_bounds__(kSortThreads) void accumulate_kernel(
         follower_short_runs<IdT, G, M, VEC>(sm.fol, ids, n, num_embeddings, id_base,
                                             skip_outside != 0, pos_bits, grad, grad_stride,
                                             main_grad, mg_stride, hidden, tiles,
-                                            (int)blockIdx.x - 1, (int)gridDim.x - 1);
+                                            (int)blockIdx.x - 1, (int)gridDim.x - 1,
+                                            &hdr->check_failures);
     }
     __syncthreads();   // the LDS of phases 1 and 2 is free from here on
     // phase 3 (a test setting keeps odd workgroups out of it)

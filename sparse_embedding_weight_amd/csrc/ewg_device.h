@@ -181,6 +181,26 @@ __device__ __forceinline__ uint32_t fetch_add_coherent(uint32_t *p, uint32_t v) 
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Device-side bounds checks, compiled in with -DEWG_DEVICE_CHECKS=1 (off by
+// default): an index at or past its bound is counted in the workspace
+// header's check_failures word and replaced by the last valid index, so that
+// a checked build never accesses memory out of bounds.
+#ifndef EWG_DEVICE_CHECKS
+#define EWG_DEVICE_CHECKS 0
+#endif
+template <typename I>
+__device__ __forceinline__ I checked_index(I i, I bound, int32_t *failures) {
+    if constexpr (EWG_DEVICE_CHECKS != 0) {
+        if (!(i < bound)) {
+            __hip_atomic_fetch_add(failures, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return bound - 1;
+        }
+    }
+    (void)bound;
+    (void)failures;
+    return i;
+}
+
 // Finish one element of a run: total = the ordered sum of its chunk sums.
 // Round once to grad's dtype, add to main_grad in fp32, round to its dtype.
 template <typename G, typename M>

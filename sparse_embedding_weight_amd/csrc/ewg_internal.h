@@ -43,7 +43,8 @@ struct WsHeader {
     uint32_t pub_long_runs;   // long runs of this call
     int32_t wait_timeouts;    // bounded waits that gave up, and records that did not
                               // belong to the call (never expected)
-    int32_t pad1[27];
+    int32_t check_failures;   // device-side bounds checks that failed (checked builds only)
+    int32_t pad1[26];
     // line 2: next column block of a long run to hand out
     uint32_t block_ticket;
     int32_t pad2[31];
@@ -55,6 +56,8 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
 static_assert(offsetof(WsHeader, wait_timeouts) == EWG_WS_WAIT_TIMEOUTS_OFFSET,
+              "documented diagnostic word");
+static_assert(offsetof(WsHeader, check_failures) == EWG_WS_CHECK_FAILURES_OFFSET,
               "documented diagnostic word");
 
 // Optional outputs of the sort step (all null in the accumulate path).

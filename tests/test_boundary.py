@@ -49,6 +49,7 @@ def test_binding_constants_match_the_header():
         "EWG_MIN_TOKENS": B.MIN_TOKENS, "EWG_MAX_TOKENS": B.MAX_TOKENS, "EWG_NROWS": B.NROWS,
         "EWG_MANY_MAX_TOKENS": B.MANY_MAX_TOKENS, "EWG_MANY_MAX_EMBEDDINGS": B.MANY_MAX_EMBEDDINGS,
         "EWG_WS_WAIT_TIMEOUTS_OFFSET": B.WS_WAIT_TIMEOUTS_OFFSET,
+        "EWG_WS_CHECK_FAILURES_OFFSET": B.WS_CHECK_FAILURES_OFFSET,
         "EWG_INT32": B.EWG_INT32, "EWG_INT64": B.EWG_INT64, "EWG_BF16": B.EWG_BF16,
         "EWG_FP32": B.EWG_FP32, "EWG_OK": B.EWG_OK, "EWG_UNSUPPORTED": B.EWG_UNSUPPORTED,
         "EWG_INVALID_ARGUMENT": B.EWG_INVALID_ARGUMENT,
