@@ -880,6 +880,10 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
     const uint32_t n_lc = min(s_word[1], n_lc_max), n_lr = min(s_word[2], n_lr_max);
     __syncthreads();   // every thread has read s_word before it is reused
     if (!take || n_blocks == 0u || n_lr == 0u) return;   // uniform
+    // the first claim goes out before the records are loaded, so that the two
+    // round trips overlap
+    uint32_t first_claim = 0u;
+    if (tid == 0) first_claim = fetch_add_coherent(&hdr->block_ticket, 1u);
     for (uint32_t r = (uint32_t)tid; r < n_lr; r += kSortThreads)
         bs.runs[r] = load_coherent16(runs_rs, r * (uint32_t)kRunRecordBytes);
     uint32_t bad = 0u;
@@ -899,7 +903,7 @@ __device__ __forceinline__ void long_blocks(BlockSmem &bs, uint32_t *s_word,
         }
     }
     if (bad) atomicOr(&s_word[3], 1u);
-    if (tid == 0) s_word[0] = fetch_add_coherent(&hdr->block_ticket, 1u);
+    if (tid == 0) s_word[0] = first_claim;
     __syncthreads();
     const bool staged_ok = s_word[3] == 0u;   // s_word[3] is not written again
     uint32_t b = s_word[0];
