@@ -5,7 +5,7 @@ On the five generated workloads at full size and on the edge cases of the
 sort (one id everywhere, every id distinct), the checked build must count no
 failed check in the workspace word at EWG_WS_CHECK_FAILURES_OFFSET and give
 main_grad bit-identical to the default build's. The checks clamp any index
-that fails them, so this build accesses no memory out of bounds either way.
+that fails them, so the checked library accesses no memory out of bounds either way.
 """
 import ctypes
 import os
