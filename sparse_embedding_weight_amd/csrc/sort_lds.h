@@ -222,13 +222,18 @@ __device__ __forceinline__ int radix_sort_ids(SortSmem &sm, int pos_bits, int id
             for (int i = 0; i < kSortItems; ++i) rank[i] = (uint32_t)(i * 64 + lane);
             if (lane == 0) cnt[mask] = (uint32_t)kWaveSlots;   // after the clearing above
         } else {
-        // lanes of the same 64-key group with the same digit (8 groups in flight)
+        // lanes of the same 64-key group with the same digit (8 groups in
+        // flight): per bit, m is all ones where the lane's bit is set and
+        // every lane keeps the peers whose ballot bit equals its own,
+        // peers & ~(m ^ ballot) on each 32-bit half (one v_bitop3 on gfx950)
         for (int b = 0; b < bits; ++b) {
 #pragma unroll
             for (int i = 0; i < kSortItems; ++i) {
-                const bool set = (dig[i] >> b) & 1u;
-                const uint64_t bal = __ballot(set);
-                peers[i] &= set ? bal : ~bal;
+                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)dig[i], b, 1);
+                const uint64_t bal = __ballot(m != 0u);
+                const uint32_t lo = (uint32_t)peers[i] & ~(m ^ (uint32_t)bal);
+                const uint32_t hi = (uint32_t)(peers[i] >> 32) & ~(m ^ (uint32_t)(bal >> 32));
+                peers[i] = ((uint64_t)hi << 32) | lo;
             }
         }
         // The lowest lane of each digit adds the digit's keys of the group to
