@@ -21,15 +21,17 @@ constexpr int kMaxCombineCols = 8192;    // columns of one combine block (8 per 
 
 // Columns of one combine task for a run of `chunks` chunk sums: the widest
 // multiple of 64 columns that lets the whole run fit the staging buffer of
-// STAGE floats, at
-// least 64, at most kMaxCombineCols and at most hidden rounded up to 64. Deep
-// runs get narrow tasks (many in parallel, one load round trip each), shallow
-// runs one task for all columns.
+// STAGE floats, at least kMinCombineCols, at most kMaxCombineCols and at most
+// hidden rounded up to 64. Deep runs get narrow tasks (many in parallel, one
+// load round trip each, or two at the minimum width), shallow runs one task
+// for all columns. (A minimum of 64 columns, 256-byte pieces of each partial
+// row, took the many-token call on 32768 tokens ~1 µs longer.)
+constexpr int kMinCombineCols = 128;
 template <int STAGE = kStageFloats>
 __device__ __forceinline__ int combine_width(int chunks, int hidden) {
     int w = STAGE / (chunks > 1 ? chunks : 1);
     w = w / 64 * 64;
-    w = w < 64 ? 64 : (w > kMaxCombineCols ? kMaxCombineCols : w);
+    w = w < kMinCombineCols ? kMinCombineCols : (w > kMaxCombineCols ? kMaxCombineCols : w);
     const int h = (hidden + 63) / 64 * 64;
     return w < h ? w : h;
 }

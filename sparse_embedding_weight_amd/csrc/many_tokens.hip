@@ -63,7 +63,7 @@ constexpr int kCombineGroupsPerCu = 4;     // combine_kernel workgroups per comp
 // Word per sorted rank: 0, or the first row of a chunk: bit 0 set, rows - 1
 // in bits 1..4, bit 5 if the run has more than 10 rows, bit 6 if the chunk is
 // the run's first; the first chunk of a long run carries the run's number of
-// combine tasks from bit 8 (at most ceil(hidden / 64) <= 2^18).
+// combine tasks from bit 8 (at most ceil(hidden / 128) <= 2^17).
 constexpr uint32_t kHeadChunk = 1u, kHeadLong = 1u << 5, kHeadRun = 1u << 6;
 constexpr int kTasksShift = 8;
 constexpr uint32_t kHeadLongRun = kHeadChunk | kHeadLong | kHeadRun;
