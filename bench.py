@@ -435,6 +435,10 @@ def measure(torch, ewg, B, hip, work, args, flush, flush_sink):
         "GB_per_s": round(work.alg_bytes / (call_ms * 1e-3) / 1e9, 1),
         "us_per_launch": round(kernel_ms * 1e3, 2), "us_per_launch_p10_p50_p90": pct(t_kernel),
         "kernel_GB_per_s": round(kernel_gbs, 1), "frac": round(kernel_gbs / PEAK_HBM_GBS, 4),
+        # the same at the median launch: a memory-system stall of one launch in
+        # tens (~20-120 us longer) moves the mean of 50 but not the median
+        "frac_at_median_launch": round(
+            work.alg_bytes / (float(np.median(t_kernel)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "traffic": measured_traffic(work.name),
     })
     return rec, call_ms, kernel_ms, wall
